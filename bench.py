@@ -1,0 +1,281 @@
+"""Benchmark one paged GQA decode step on one MI355X.
+
+Default workload: the single long context (B=1, Hq=32, Hkv=8, d=128,
+32768 tokens, bf16, 4096-page shuffled pool, S=32 split). Prints ONE JSON
+line. The step time is the GPU span of the step (HIP events recorded on the
+launch stream before the partial kernel and after the merge kernel),
+averaged over the timed steps; ``value`` is the step's algorithmic bytes
+(K/V of the exact tokens + q + out + used block-table entries + seq_lens)
+divided by that time.
+
+Inputs are made once and stay in HBM. To keep the 256 MB Infinity Cache from
+serving repeated steps, the timed loop rotates over several identical copies
+of the pools (so each copy is evicted by the others before it is read again).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
+                       [--mode split] [--splits 32] [--chunk 0] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged GQA decode µs/step + effective HBM GB/s (% of MI355X peak)"
+PEAK_HBM_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+# ---------------------------------------------------------------- HIP events
+
+class HipEvents:
+    """Raw hipEvent_t handles via libamdhip64 (timing only)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+# ---------------------------------------------------------------- workload
+
+def make_inputs(name, seed, device):
+    import workloads as W
+    spec = W.CONFIGS[name]
+    if name == "b64":
+        dev = W.make_device_case(name, seed, device=device)
+        return spec, dev, None
+    case = W.make_case(name, seed, poison=False)
+    dev = W.case_to_device(case, device=device)
+    dev.update(seq_lens_host=case.seq_lens, block_table_host=case.block_table,
+               num_pages=case.num_pages, sm_scale=case.sm_scale, spec=spec)
+    return spec, dev, case
+
+
+def partial_kernel_bytes(stats, spec, batch):
+    """Algorithmic bytes the partial kernel moves per launch: K/V of the exact
+    tokens, q, used block-table entries, seq_lens (plus out when unsplit)."""
+    d, Hq = spec.head_dim, spec.num_q_heads
+    out_bytes = batch * Hq * d * 2
+    b = stats["algorithmic_bytes"] - out_bytes
+    return b + (out_bytes if stats["mode_name"] == "unsplit" else 0)
+
+
+def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev):
+    import torch
+    B = len(dev["seq_lens_host"])
+    shape = P.make_shape(B, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                         dev["block_table_host"].shape[1], dev["num_pages"], spec.dtype,
+                         dev["sm_scale"])
+    plan = P.Plan(shape, dev["seq_lens_host"], P.make_opts(mode, splits, chunk))
+    plan.upload()
+    stats = plan.stats()
+    out = torch.empty_like(dev["q"])
+    pools = dev["replicas"][:replicas]
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = ev.create(3 * steps)
+    args = lambda r: (dev["q"], pools[r][0], pools[r][1], dev["block_table"], dev["seq_lens"], out)
+    for i in range(warmup):
+        P.pkv_decode(plan.handle, *args(i % len(pools)), stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = evs[3 * i:3 * i + 3]
+        P.pkv_decode_marked(plan.handle, *args(i % len(pools)), stream, e[0], e[1], e[2])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part = [ev.ms(evs[3 * i], evs[3 * i + 1]) for i in range(steps)]
+    step = [ev.ms(evs[3 * i], evs[3 * i + 2]) for i in range(steps)]
+    ev.destroy(evs)
+    # synchronized wall time of a step including host planning + upload
+    sync = []
+    for i in range(min(20, steps)):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        plan.update(dev["seq_lens_host"])
+        plan.upload()
+        P.pkv_decode(plan.handle, *args(i % len(pools)), stream)
+        torch.cuda.synchronize()
+        sync.append(time.perf_counter() - t)
+    plan.close()
+    return {
+        "stats": stats,
+        "step_us": float(np.mean(step)) * 1e3,
+        "step_us_p10": float(np.percentile(step, 10)) * 1e3,
+        "step_us_p90": float(np.percentile(step, 90)) * 1e3,
+        "partial_us": float(np.mean(part)) * 1e3,
+        "wall_us_per_step": wall / steps * 1e6,
+        "sync_wall_us_with_plan": float(np.median(sync)) * 1e6,
+    }
+
+
+def cpu_baseline(case, target_s=10.0, cap_s=30.0):
+    """Time the CPU oracle on the bench workload until ~target_s of work."""
+    from oracle import paged_gqa as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t = time.perf_counter()
+        O.decode_case(case)
+        times.append(time.perf_counter() - t)
+        el = time.perf_counter() - t_start
+        if el >= target_s or el + times[-1] > cap_s:
+            break
+    return float(np.median(times)), len(times), threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="long")
+    ap.add_argument("--mode", default=None)
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-auto", action="store_true")
+    a = ap.parse_args()
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.stderr.write("bench.py measures one GPU only: this library has no "
+                         "multi-GPU path (run with --gpus 1)\n")
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_gqa_04_amd as P
+    import workloads as W
+
+    seed = W.SEED_HOLDOUT if a.seed is None else a.seed
+    torch.cuda.set_device(0)
+    spec, dev, case = make_inputs(a.config, seed, "cuda")
+    mode = a.mode or spec.mode
+    splits = a.splits if a.splits is not None else (spec.num_splits or 0)
+    if mode != "split":
+        splits = a.splits or 0
+
+    touched = int(np.sum(dev["seq_lens_host"])) * spec.num_kv_heads * spec.head_dim * 4
+    replicas = a.replicas or (1 if touched > 4 * MALL_BYTES else
+                              min(8, math.ceil(2 * MALL_BYTES / max(1, touched)) + 1))
+    reps = [(dev["k_pool"], dev["v_pool"])]
+    for _ in range(replicas - 1):
+        reps.append((dev["k_pool"].clone(), dev["v_pool"].clone()))
+    dev["replicas"] = reps
+    ev = HipEvents()
+
+    r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev)
+    st = r["stats"]
+    B = len(dev["seq_lens_host"])
+    alg = st["algorithmic_bytes"]
+    gbps = alg / (r["step_us"] * 1e-6) / 1e9
+    part_bytes = partial_kernel_bytes(st, spec, B)
+    part_gbps = part_bytes / (r["partial_us"] * 1e-6) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["step_us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name, "description": spec.description, "batch": B,
+            "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim, "page_size": 16,
+            "kv_tokens": int(st["kv_tokens"]), "pool_pages": int(dev["num_pages"]),
+            "mode": st["mode_name"], "num_splits": st["num_splits"],
+            "chunk_pages": st["chunk_pages"], "seed": seed, "pool_replicas": replicas,
+        },
+        "us_per_step": round(r["step_us"], 2),
+        "us_per_step_p10_p90": [round(r["step_us_p10"], 2), round(r["step_us_p90"], 2)],
+        "pct_of_peak_hbm": round(100 * gbps / PEAK_HBM_GBPS, 1),
+        "algorithmic_bytes_per_step": int(alg),
+        "wall_us_per_step": round(r["wall_us_per_step"], 2),
+        "sync_wall_us_with_plan": round(r["sync_wall_us_with_plan"], 2),
+        "roofline": {
+            "kernel": "partial_kernel",
+            "bound": "hbm",
+            "achieved": round(part_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(part_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(part_bytes),
+            "avg_launch_us": round(r["partial_us"], 2),
+        },
+        "scheduler": {k: st[k] for k in ("grid", "num_items", "empty_items", "num_slots",
+                                         "launches", "bucket_launches", "partial_bytes",
+                                         "upload_bytes")},
+    }
+    if not a.no_auto and mode != "auto":
+        ra = time_mode(P, dev, spec, "auto", 0, 0, a.steps, a.warmup, replicas, ev)
+        sa = ra["stats"]
+        line["auto"] = {
+            "mode": sa["mode_name"], "num_splits": sa["num_splits"],
+            "chunk_pages": sa["chunk_pages"], "grid": sa["grid"],
+            "us_per_step": round(ra["step_us"], 2),
+            "gbps": round(sa["algorithmic_bytes"] / (ra["step_us"] * 1e-6) / 1e9, 1),
+        }
+    if not a.no_cpu and case is not None:
+        sec, reps_done, threads = cpu_baseline(case)
+        line["cpu_baseline"] = {
+            "value": round(alg / sec / 1e9, 3),
+            "unit": "GB/s",
+            "us_per_step": round(sec * 1e6, 1),
+            "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"whole {spec.name} step (all {B} sequence(s) x {spec.num_kv_heads} "
+                      f"KV heads), float64 numpy oracle, median of {reps_done} runs",
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

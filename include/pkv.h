@@ -1,0 +1,251 @@
+/*
+ * pkv.h -- C ABI of a paged grouped-query-attention (GQA) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode step: every sequence b contributes one query token per query
+ * head; it attends over the N_b tokens already in a paged KV cache. The cache
+ * is read in place through a block table, never repacked (PersistentKV
+ * explainer, Technical summary > Methodology 1, layout). Query heads are
+ * grouped: G = Hq / Hkv query heads share one KV head, head h reading KV head
+ * h / G (same section, the GQA definition).
+ *
+ * The step is planned on the host and run by hand-written HIP kernels:
+ *
+ *   pkv_plan_create / pkv_plan_update   host, integer only: pick the mode
+ *       (unsplit, split-S, work queue), cut each (sequence, KV head) into
+ *       page-aligned ranges from the real per-row lengths, and build the
+ *       compact work queue (Methodology 1, sequence splitting, row-local
+ *       bounds, compact workqueue; Methodology 2, calibrated policy).
+ *   pkv_plan_upload    binds the caller's workspace and copies the queue.
+ *   pkv_decode         launches the partial kernel (one workgroup per range;
+ *       each writes a partial online-softmax state (m, l, acc) or, unsplit,
+ *       the output) and, when ranges were split, the merge kernel that
+ *       combines the states exactly.
+ *
+ * Data layouts (all device memory, row-major, owned by the caller):
+ *   q, out        [B, Hq, d]                 dtype (fp16 or bf16)
+ *   k_pool,v_pool [num_pages, Hkv, P, d]     dtype; P = 16 tokens per page.
+ *                 One (page, KV head) tile is P*d contiguous elements.
+ *   block_table   int32 [B, block_table_stride]; entry j of row b is the
+ *                 physical page holding logical tokens [j*P, (j+1)*P) of
+ *                 sequence b (LLM Primer ch. 8, section 8.1). Entries at or
+ *                 beyond ceil(N_b / P) are never read.
+ *   seq_lens      int32 [B]; N_b >= 0. Must hold the same values as the host
+ *                 array the plan was built from.
+ * Tail slots of a sequence's last page (t >= N_b) may hold anything,
+ * including NaN: they never reach the arithmetic.
+ *
+ * Numerics: products and sums in fp32; out = acc / l rounded to nearest even
+ * in the storage dtype. sm_scale multiplies q.k before the softmax.
+ *
+ * Errors: every call returns a pkv_status; nothing aborts and no C++
+ * exception crosses the ABI. pkv_last_error() gives a thread-local message
+ * for the last failing call on the calling thread.
+ *
+ * Threading and streams: plans are host objects, not internally locked; use
+ * one plan from one thread at a time. pkv_decode is asynchronous on the
+ * caller's stream and does not synchronise. Decodes of different plans with
+ * different workspaces may overlap; two decodes sharing one workspace must be
+ * ordered by the caller (the same stream does that).
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* bad argument: null, negative, inconsistent */
+  PKV_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, G, page size */
+  PKV_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
+  PKV_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_STATE = -5        /* call out of order (e.g. decode before upload) */
+} pkv_status;
+
+/* Storage dtype shared by q, the K/V pools and out. */
+typedef enum pkv_dtype { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Dispatch modes (PersistentKV explainer, Methodology 2: the policy routes a
+ * step to one of several execution paths by batch size and length).
+ *   UNSPLIT    one workgroup per (sequence, KV head); writes out; 1 launch.
+ *   SPLIT      rectangular grid B x Hkv x S; row b uses
+ *              chunk_b = ceil(pages_b / S) pages per range; cells past the
+ *              row's last range write a neutral state; partial + merge.
+ *   WORKQUEUE  1-D grid over the non-empty (sequence, KV head, range) items
+ *              only, every range chunk_pages pages long (the last one of a
+ *              row shorter); partial + merge.
+ *   AUTO       the calibrated policy picks one of the three. */
+typedef enum pkv_mode {
+  PKV_MODE_AUTO = 0,
+  PKV_MODE_UNSPLIT = 1,
+  PKV_MODE_SPLIT = 2,
+  PKV_MODE_WORKQUEUE = 3
+} pkv_mode;
+
+/* Problem shape. Supported: page_size 16; head_dim 64 or 128;
+ * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
+typedef struct pkv_shape {
+  int32_t batch;              /* B >= 0 */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;           /* d */
+  int32_t page_size;          /* P, tokens per page */
+  int32_t block_table_stride; /* int32 entries per block_table row */
+  int64_t num_pages;          /* pool capacity in pages (both pools) */
+  int32_t dtype;              /* pkv_dtype */
+  float sm_scale;             /* softmax scale; 0 selects 1/sqrt(d) */
+} pkv_shape;
+
+/* Planning options; zero-initialised means "automatic" everywhere. */
+typedef struct pkv_opts {
+  int32_t mode;        /* pkv_mode */
+  int32_t num_splits;  /* SPLIT: S (0 = policy's choice) */
+  int32_t chunk_pages; /* WORKQUEUE: pages per range (0 = policy's choice) */
+  int32_t num_cus;     /* compute units to plan for (0 = ask the device) */
+  uint32_t queue_seed; /* 0: longest ranges first; else a seeded shuffle of
+                          the queue (results do not depend on queue order) */
+  int32_t reserved[3];
+} pkv_opts;
+
+/* Scheduler-derived counters of one planned step (PersistentKV explainer,
+ * Technical summary > Results: launch fan-out and merge-state traffic). */
+typedef struct pkv_plan_stats {
+  int32_t mode;            /* resolved pkv_mode (never AUTO) */
+  int32_t num_splits;      /* S: most ranges any (sequence, KV head) has */
+  int32_t chunk_pages;     /* pages per range (SPLIT: the largest row's) */
+  int32_t grid;            /* partial-kernel workgroups launched */
+  int32_t num_items;       /* launched workgroups that read KV */
+  int32_t empty_items;     /* launched workgroups that only write a neutral
+                              state (SPLIT cells past a row's end) */
+  int32_t num_slots;       /* partial states written and merged */
+  int32_t launches;        /* kernel launches per step: 1 or 2 */
+  int32_t bucket_launches; /* launches exact-length bucketing would issue:
+                              one partial + one merge per distinct N_b > 0 */
+  int32_t reserved;
+  int64_t kv_tokens;         /* sum of N_b */
+  int64_t algorithmic_bytes; /* K/V of the N_b tokens + q + out + used
+                                block-table entries + seq_lens */
+  int64_t partial_bytes;     /* merge-state traffic: bytes of (m, l, acc)
+                                written by the partial kernel + read by the
+                                merge kernel */
+  int64_t upload_bytes;      /* host-to-device bytes per step (the queue) */
+  int64_t workspace_bytes;   /* what pkv_plan_workspace_bytes returns */
+} pkv_plan_stats;
+
+/* Where the partial states sit in the workspace, for inspection in tests.
+ * Slot of (b, g, s): WORKQUEUE  slot_base[b] + g * S_b + s, with
+ * (slot_base[b], S_b) the int32 pair at meta_offset + 8*b;
+ * SPLIT  (b * Hkv + g) * S + s. Per slot: m_log2[G] (the reference maximum,
+ * in log2 units of the scaled logits: m_log2 = m * log2(e)), l[G] and
+ * acc[G][d], all fp32; the state is (m, l, acc) with l = sum exp(x - m) and
+ * acc = sum exp(x - m) v over the range; a neutral state is
+ * (-inf, 0, 0). m need not be the range's exact maximum: any reference at
+ * or above it by a bounded amount represents the same state. */
+typedef struct pkv_workspace_layout {
+  int64_t items_offset;  /* int32x4 {b*Hkv+g, page_begin, page_end, slot} */
+  int64_t meta_offset;   /* int32x2 per sequence (WORKQUEUE) */
+  int64_t m_offset;      /* fp32 [num_slots][G] */
+  int64_t l_offset;      /* fp32 [num_slots][G] */
+  int64_t acc_offset;    /* fp32 [num_slots][G][d] */
+  int64_t total_bytes;
+  int32_t num_items;
+  int32_t num_slots;
+  int32_t group;         /* G */
+  int32_t num_splits;    /* S */
+} pkv_workspace_layout;
+
+typedef struct pkv_plan pkv_plan; /* opaque; host-owned */
+
+/* Build a plan for one decode step.
+ *   shape          problem shape (copied).
+ *   seq_lens_host  int32[batch] host array of N_b (copied; may be NULL when
+ *                  batch == 0).
+ *   opts           may be NULL (all automatic).
+ *   out_plan       receives the new plan; *out_plan is NULL on failure.
+ * Errors: PKV_ERR_INVALID for null pointers, negative sizes, Hq % Hkv != 0,
+ * N_b < 0 or N_b > block_table_stride * page_size; PKV_ERR_UNSUPPORTED for a
+ * page size, head_dim, G or dtype this build has no kernel for; PKV_ERR_HIP
+ * if num_cus is 0 and the device cannot be queried. Host-only: calls no HIP
+ * function unless num_cus is 0. */
+pkv_status pkv_plan_create(const pkv_shape* shape, const int32_t* seq_lens_host,
+                           const pkv_opts* opts, pkv_plan** out_plan);
+
+/* Re-plan in place for the next step (same shape and options, new lengths);
+ * reuses the plan's host buffers. Waits for the plan's previous upload copy
+ * to leave its pinned staging buffer. The plan must be uploaded again before
+ * the next decode. Errors as pkv_plan_create. (Serving re-forms the batch
+ * every step: ai-trend study note, "How it works", step four.) */
+pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* seq_lens_host);
+
+/* Device workspace the plan needs (bytes, 0 for UNSPLIT). */
+size_t pkv_plan_workspace_bytes(const pkv_plan* plan);
+
+/* Bind a caller-owned device workspace of at least
+ * pkv_plan_workspace_bytes() bytes (256-byte aligned) and enqueue the copy of
+ * the work queue into it on `stream`. The workspace must stay allocated
+ * until every decode that uses it has finished on the device. Errors:
+ * PKV_ERR_WORKSPACE (null when needed, too small, misaligned), PKV_ERR_HIP. */
+pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Copy the plan's counters. */
+pkv_status pkv_plan_stats_get(const pkv_plan* plan, pkv_plan_stats* stats);
+
+/* Describe where the partial states live in the workspace. */
+pkv_status pkv_plan_layout_get(const pkv_plan* plan,
+                               pkv_workspace_layout* layout);
+
+/* Copy the host image of what pkv_plan_upload sends: the work-queue items
+ * (int32x4 {b*Hkv+g, page_begin, page_end, slot} at items_offset) and the
+ * per-sequence (slot_base, S_b) pairs at meta_offset, laid out exactly as in
+ * the workspace. `bytes` must be at least meta_offset + 8*batch (0 is fine
+ * when the plan uploads nothing). For inspection and tests. */
+pkv_status pkv_plan_queue_get(const pkv_plan* plan, void* dst, size_t bytes);
+
+/* Run one decode step on `stream` (asynchronous).
+ *   q, k_pool, v_pool, out: device pointers, 16-byte aligned, layouts above.
+ *   block_table, seq_lens:  device int32 arrays, 4-byte aligned.
+ * Block-table entries are not trusted blindly: a page index outside
+ * [0, num_pages) contributes no tokens instead of being read.
+ * Errors: PKV_ERR_INVALID (null or misaligned pointer), PKV_ERR_STATE (plan
+ * not uploaded), PKV_ERR_HIP (launch failure). */
+pkv_status pkv_decode(const pkv_plan* plan, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table,
+                      const int32_t* seq_lens, void* out, hipStream_t stream);
+
+/* pkv_decode with timing marks: records `before` ahead of the partial
+ * kernel, `after_partial` after it and `after_merge` after the merge kernel
+ * (or after the partial kernel when there is no merge), each on `stream`.
+ * Any event may be NULL. Used to time the partial kernel on its own stream. */
+pkv_status pkv_decode_marked(const pkv_plan* plan, const void* q,
+                             const void* k_pool, const void* v_pool,
+                             const int32_t* block_table,
+                             const int32_t* seq_lens, void* out,
+                             hipStream_t stream, hipEvent_t before,
+                             hipEvent_t after_partial, hipEvent_t after_merge);
+
+/* Free a plan (NULL is a no-op). Waits for its last upload copy. */
+void pkv_plan_destroy(pkv_plan* plan);
+
+/* Static string naming a status code. */
+const char* pkv_status_string(int32_t status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,725 @@
+// Paged GQA decode kernels for gfx950 (MI355X) and their dispatch.
+//
+// Partial kernel: one workgroup per (sequence b, KV head g, page range).
+// Reads the range's K/V pages straight from the pools through the block
+// table (PersistentKV explainer, Technical summary > Methodology 1: the
+// engine runs on the paged layout without repacking), computes the G x 16
+// logits of each page, keeps an online-softmax state and accumulates P.V in
+// fp32. The state of the range is written as a partial (m, l, acc) for the
+// merge kernel, or, when the range is the whole row, normalised into out.
+//
+// Merge kernel: one wave per (sequence, query head); combines the row's
+// partial states in split-index order: M = max m_s, weights exp(m_s - M),
+// out = sum w_s acc_s / sum w_s l_s (Methodology 1, the separate merge
+// kernel that combines the states exactly).
+//
+// The step is HBM-bound: every K/V byte is read once and each element feeds
+// only G multiply-adds (ai-trend study note, "Why it was needed": decode reads
+// the whole KV cache per token and is bandwidth bound).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescaling slack (log2 units): the running reference maximum is only
+// raised when a logit exceeds it by more than this, so exponentials stay
+// below 2^8 and the accumulator is rescaled rarely.
+constexpr float kTau = 8.0f;
+// Initial reference maximum: finite, so exp2(x - ref) of a masked logit
+// (-inf) is 0 and never NaN; far below any real logit.
+constexpr float kNoMax = -1.0e30f;
+constexpr int kThreads = kWavesPerGroup * 64;
+
+// ---------------------------------------------------------------- helpers
+
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
+                                  __builtin_bit_cast(f16x2_t, b), c, false);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t u, float& lo, float& hi) {
+  if constexpr (DT == PKV_BF16) {
+    lo = __uint_as_float(u << 16);
+    hi = __uint_as_float(u & 0xffff0000u);
+  } else {
+    f16x2_t h = __builtin_bit_cast(f16x2_t, u);
+    lo = (float)h[0];
+    hi = (float)h[1];
+  }
+}
+
+// fp32 -> storage, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint16_t pack1(float f) {
+  if constexpr (DT == PKV_BF16) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 4 or 8), result in
+// every lane of the group. DPP: quad_perm [1,0,3,2], [2,3,0,1], then
+// row_half_mirror pairs the two quads of each 8-lane half.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  if constexpr (N == 8) v += dpp_mov<0x141>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// ------------------------------------------------------------- parameters
+
+struct PartialParams {
+  const uint16_t* __restrict__ q;
+  const uint16_t* __restrict__ k_pool;
+  const uint16_t* __restrict__ v_pool;
+  const int32_t* __restrict__ block_table;
+  const int32_t* __restrict__ seq_lens;
+  uint16_t* __restrict__ out;
+  const Item* __restrict__ items;
+  float* __restrict__ ws_m;
+  float* __restrict__ ws_l;
+  float* __restrict__ ws_acc;
+  int64_t num_pages;
+  int32_t stride;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t mode;
+  int32_t num_splits;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* __restrict__ ws_m;
+  const float* __restrict__ ws_l;
+  const float* __restrict__ ws_acc;
+  const SeqMeta* __restrict__ meta;
+  uint16_t* __restrict__ out;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t group;
+  int32_t mode;
+  int32_t num_splits;
+};
+
+// ---------------------------------------------------------- partial kernel
+//
+// Lane layouts inside a wave, for one 16-token page of one KV head (the
+// page tile is 16 x D contiguous elements):
+//  * K: LPT lanes per token (4, or 8 when D = 128 and G = 8); lane
+//    (t = lane / LPT, c = lane % LPT) holds elements
+//    {j*8*LPT + c*8 + i} of its token, so each 16-byte load instruction reads
+//    whole 64- or 128-byte runs of every token row. A page takes
+//    16*LPT/64 passes. q is held in the same layout, so q.k is D/LPT/2
+//    v_dot2 per head, then an LPT-lane DPP sum.
+//  * V: D/8 lanes per token; lane (r = lane / (D/8), c = lane % (D/8)) holds
+//    elements c*8 .. c*8+7, so one load instruction reads 64 consecutive
+//    16-byte pieces (1 KiB). acc[G][8] per lane; lanes with equal c and
+//    different r are summed once at the end of the range.
+//  * p (softmax weights) moves from the K layout to the V layout through a
+//    small per-wave LDS buffer.
+// Each wave keeps a wave-uniform reference maximum per head; it is raised
+// (with a rescale of l and acc) only when a logit exceeds it by kTau.
+template <int DT, int G, int D>
+__global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
+  constexpr int W = kWavesPerGroup;
+  constexpr int P = kPageTokens;
+  constexpr int LPT = (D == 128 && G >= 8) ? 8 : 4;
+  constexpr int EK = D / LPT;    // K elements per lane per pass
+  constexpr int NKL = EK / 8;    // 16-byte K loads per lane per pass
+  constexpr int TPK = 64 / LPT;  // tokens per K pass
+  constexpr int NKP = P / TPK;   // K passes per page
+  constexpr int VL = D / 8;      // lanes per token in the V layout
+  constexpr int TPI = 64 / VL;   // tokens per V load instruction
+  constexpr int NVI = P / TPI;   // V loads per lane per page
+  constexpr int TILE = P * D;    // elements of one (page, KV head) tile
+
+  __shared__ float s_p[W][P * G];
+  __shared__ float s_m[W][G];
+  __shared__ float s_l[W][G];
+  __shared__ float s_acc[W][G * D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int Hkv = a.num_kv_heads;
+
+  // ---- which range this workgroup owns ----
+  int b, g, pb, pe, slot = 0;
+  if (a.mode == PKV_MODE_WORKQUEUE) {
+    const Item it = a.items[blockIdx.x];
+    b = it.bg / Hkv;
+    g = it.bg - b * Hkv;
+    pb = it.page_begin;
+    pe = it.page_end;
+    slot = it.slot;
+  } else if (a.mode == PKV_MODE_SPLIT) {
+    const int S = a.num_splits;
+    const int cell = blockIdx.x;
+    const int s = cell % S;
+    const int bg = cell / S;
+    b = bg / Hkv;
+    g = bg - b * Hkv;
+    const int pages = (a.seq_lens[b] + P - 1) / P;
+    const int chunk = pages > 0 ? (pages + S - 1) / S : 1;  // row-local
+    pb = s * chunk;
+    pe = min(pb + chunk, pages);
+    slot = cell;
+  } else {
+    b = blockIdx.x / Hkv;
+    g = blockIdx.x - b * Hkv;
+    pb = 0;
+    pe = 0x7fffffff;
+  }
+  const int n = a.seq_lens[b];
+  // Never past the device's own length, nor past the block-table row.
+  pe = min(pe, min((n + P - 1) / P, a.stride));
+
+  if (pb >= pe) {
+    // Empty range: neutral state (or zeros for an empty row), read nothing.
+    for (int e = threadIdx.x; e < G * D; e += kThreads) {
+      const int h = e / D, dd = e - h * D;
+      if (a.mode == PKV_MODE_UNSPLIT) {
+        a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] = 0;
+      } else {
+        a.ws_acc[((int64_t)slot * G + h) * D + dd] = 0.0f;
+        if (dd == 0) {
+          a.ws_m[(int64_t)slot * G + h] = -INFINITY;
+          a.ws_l[(int64_t)slot * G + h] = 0.0f;
+        }
+      }
+    }
+    return;
+  }
+
+  const int kt = lane / LPT, kc = lane % LPT;
+  const int vr = lane / VL, vc = lane % VL;
+
+  // q of the group's G heads, in the K layout (packed pairs).
+  uint32_t qr[G][EK / 2];
+  {
+    const uint16_t* qb = a.q + ((int64_t)b * a.num_q_heads + g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < NKL; ++j) {
+        const u32x4 v = *(const u32x4*)(qb + h * D + j * 8 * LPT + kc * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qr[h][j * 4 + w] = v[w];
+      }
+  }
+
+  float acc[G][8];
+  float lsum[G], mref[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lsum[h] = 0.0f;
+    mref[h] = kNoMax;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  }
+
+  // Pages of this wave: pb + wave + W*k, k in [0, cnt).
+  const int span = pe - pb;
+  const int cnt = span > wave ? (span - wave + W - 1) / W : 0;
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.stride + pb + wave;
+
+  // Block-table entries, 64 per vector load, read out with v_readlane.
+  auto bt_load = [&](int k0) -> int {
+    const int k = k0 + lane;
+    return k < cnt ? bt_row[(int64_t)k * W] : 0;
+  };
+  int bt_cur = bt_load(0);
+  int bt_nxt = cnt > 64 ? bt_load(64) : 0;
+  int bt_pos = 0, bt_base = 0;
+  auto next_phys = [&]() -> int {
+    if (bt_pos == 64) {
+      bt_cur = bt_nxt;
+      bt_base += 64;
+      bt_pos = 0;
+      bt_nxt = cnt > bt_base + 64 ? bt_load(bt_base + 64) : 0;
+    }
+    return __builtin_amdgcn_readlane(bt_cur, bt_pos++);
+  };
+
+  struct Page {
+    u32x4 k[NKP][NKL];
+    u32x4 v[NVI];
+    int ntok;  // valid tokens of the page (0 if its table entry is bad)
+  };
+
+  auto load_page = [&](Page& r, int k) {
+    const int lp = pb + wave + W * k;
+    int phys = next_phys();
+    const bool ok = (uint64_t)(uint32_t)phys < (uint64_t)a.num_pages;
+    r.ntok = ok ? min(P, n - lp * P) : 0;
+    phys = ok ? phys : 0;
+    const int64_t tile = ((int64_t)phys * Hkv + g) * TILE;
+    const uint16_t* kp = a.k_pool + tile;
+    const uint16_t* vp = a.v_pool + tile;
+#pragma unroll
+    for (int pk = 0; pk < NKP; ++pk)
+#pragma unroll
+      for (int j = 0; j < NKL; ++j)
+        r.k[pk][j] = *(const u32x4*)(kp + (pk * TPK + kt) * D + j * 8 * LPT + kc * 8);
+#pragma unroll
+    for (int i = 0; i < NVI; ++i)
+      r.v[i] = *(const u32x4*)(vp + (i * TPI + vr) * D + vc * 8);
+  };
+
+  float* sp = s_p[wave];
+
+  auto compute_page = [&](const Page& r) {
+    // logits, log2 domain, masked by select (never by multiply: tails may
+    // hold NaN).
+    float x[NKP][G];
+#pragma unroll
+    for (int pk = 0; pk < NKP; ++pk) {
+      const bool valid = (pk * TPK + kt) < r.ntok;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NKL; ++j)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) s = dot2<DT>(r.k[pk][j][w], qr[h][j * 4 + w], s);
+        s = group_sum<LPT>(s);
+        x[pk][h] = valid ? s * a.scale_log2 : -INFINITY;
+      }
+    }
+    bool need = false;
+#pragma unroll
+    for (int pk = 0; pk < NKP; ++pk)
+#pragma unroll
+      for (int h = 0; h < G; ++h) need |= x[pk][h] > mref[h] + kTau;
+    if (__any(need)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float pm = x[0][h];
+#pragma unroll
+        for (int pk = 1; pk < NKP; ++pk) pm = fmaxf(pm, x[pk][h]);
+        pm = wave_max(pm);
+        const float mnew = fmaxf(mref[h], pm);
+        const float alpha = fast_exp2(mref[h] - mnew);
+        lsum[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+        mref[h] = mnew;
+      }
+    }
+#pragma unroll
+    for (int pk = 0; pk < NKP; ++pk) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = fast_exp2(x[pk][h] - mref[h]);
+        x[pk][h] = p;
+        lsum[h] += p;
+      }
+      if (kc == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sp[(pk * TPK + kt) * G + h] = x[pk][h];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) {
+      const int t = i * TPI + vr;
+      float pv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[h] = sp[t * G + h];
+      float vf[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) unpack2<DT>(r.v[i][w], vf[2 * w], vf[2 * w + 1]);
+      if (r.ntok < P) {  // wave-uniform: only a row's last page is partial
+        const bool valid = t < r.ntok;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // Software pipeline: the next page's loads are in flight while the
+  // current page is computed.
+  Page buf0, buf1;
+  if (cnt > 0) load_page(buf0, 0);
+  for (int k = 0; k < cnt; k += 2) {
+    if (k + 1 < cnt) load_page(buf1, k + 1);
+    compute_page(buf0);
+    if (k + 1 >= cnt) break;
+    if (k + 2 < cnt) load_page(buf0, k + 2);
+    compute_page(buf1);
+  }
+
+  // ---- combine the wave states, then the workgroup's waves ----
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int m = LPT; m < 64; m <<= 1) lsum[h] += __shfl_xor(lsum[h], m);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int m = VL; m < 64; m <<= 1) acc[h][e] += __shfl_xor(acc[h][e], m);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_m[wave][h] = mref[h];
+      s_l[wave][h] = lsum[h];
+    }
+  }
+  if (lane < VL) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wave][h * D + lane * 8 + e] = acc[h][e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += kThreads) {
+    const int h = e / D, dd = e - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float sc = fast_exp2(s_m[w][h] - M);
+      L = fmaf(sc, s_l[w][h], L);
+      A = fmaf(sc, s_acc[w][e], A);
+    }
+    if (a.mode == PKV_MODE_UNSPLIT) {
+      a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] =
+          pack1<DT>(L > 0.0f ? A / L : 0.0f);
+    } else {
+      a.ws_acc[((int64_t)slot * G + h) * D + dd] = A;
+      if (dd == 0) {
+        a.ws_m[(int64_t)slot * G + h] = L > 0.0f ? M : -INFINITY;
+        a.ws_l[(int64_t)slot * G + h] = L;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ merge kernel
+//
+// One wave per (sequence b, query head h). Reduces the row's S_b partial
+// states in split-index order, so the result does not depend on the order
+// in which the partial kernel ran its items.
+template <int DT, int D>
+__global__ __launch_bounds__(64) void merge_kernel(MergeParams a) {
+  constexpr int E = D / 64;  // output elements per lane
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.num_q_heads;
+  const int h = bh - b * a.num_q_heads;
+  const int G = a.group;
+  const int g = h / G, hh = h - g * G;
+  int Sb, base;
+  if (a.mode == PKV_MODE_WORKQUEUE) {
+    const SeqMeta sm = a.meta[b];
+    Sb = sm.splits;
+    base = sm.slot_base + g * Sb;
+  } else {
+    Sb = a.num_splits;
+    base = (b * a.num_kv_heads + g) * Sb;
+  }
+  float M = -INFINITY;
+  for (int s = lane; s < Sb; s += 64) M = fmaxf(M, a.ws_m[(int64_t)(base + s) * G + hh]);
+  M = wave_max(M);
+  float L = 0.0f, A[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) A[e] = 0.0f;
+#pragma unroll 4
+  for (int s = 0; s < Sb; ++s) {
+    const int64_t st = (int64_t)(base + s) * G + hh;
+    const float m = a.ws_m[st];
+    const float sc = m == -INFINITY ? 0.0f : fast_exp2(m - M);
+    L = fmaf(sc, a.ws_l[st], L);
+    const float* src = a.ws_acc + st * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) A[e] = fmaf(sc, src[e], A[e]);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  uint16_t* dst = a.out + ((int64_t)b * a.num_q_heads + h) * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[e] = pack1<DT>(A[e] * inv);
+}
+
+// -------------------------------------------------------------- dispatch
+
+using PartialLaunch = void (*)(dim3, hipStream_t, const PartialParams&);
+using MergeLaunch = void (*)(dim3, hipStream_t, const MergeParams&);
+
+template <int DT, int G, int D>
+void launch_partial(dim3 grid, hipStream_t s, const PartialParams& p) {
+  hipLaunchKernelGGL((partial_kernel<DT, G, D>), grid, dim3(kThreads), 0, s, p);
+}
+
+template <int DT, int D>
+void launch_merge(dim3 grid, hipStream_t s, const MergeParams& p) {
+  hipLaunchKernelGGL((merge_kernel<DT, D>), grid, dim3(64), 0, s, p);
+}
+
+template <int DT, int D>
+PartialLaunch pick_partial_g(int G) {
+  switch (G) {
+    case 1: return launch_partial<DT, 1, D>;
+    case 2: return launch_partial<DT, 2, D>;
+    case 4: return launch_partial<DT, 4, D>;
+    case 8: return launch_partial<DT, 8, D>;
+    default: return nullptr;
+  }
+}
+
+PartialLaunch pick_partial(int dt, int G, int D) {
+  if (dt == PKV_BF16) return D == 128 ? pick_partial_g<PKV_BF16, 128>(G) : pick_partial_g<PKV_BF16, 64>(G);
+  return D == 128 ? pick_partial_g<PKV_F16, 128>(G) : pick_partial_g<PKV_F16, 64>(G);
+}
+
+MergeLaunch pick_merge(int dt, int D) {
+  if (dt == PKV_BF16) return D == 128 ? launch_merge<PKV_BF16, 128> : launch_merge<PKV_BF16, 64>;
+  return D == 128 ? launch_merge<PKV_F16, 128> : launch_merge<PKV_F16, 64>;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+pkv_status hip_fail(const char* what, hipError_t e) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return PKV_ERR_HIP;
+}
+
+pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* seq_lens, void* out,
+                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1, hipEvent_t ev2) {
+  clear_error();
+  if (!p) {
+    set_error("plan is NULL");
+    return PKV_ERR_INVALID;
+  }
+  const pkv_shape& s = p->shape;
+  if (s.batch == 0) {
+    hipError_t e = hipSuccess;
+    for (hipEvent_t ev : {ev0, ev1, ev2})
+      if (ev && (e = hipEventRecord(ev, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
+    return PKV_OK;
+  }
+  if (!q || !out || !seq_lens || (p->kv_tokens > 0 && (!k_pool || !v_pool || !block_table))) {
+    set_error("a required device pointer is NULL");
+    return PKV_ERR_INVALID;
+  }
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4)) {
+    set_error("q/out/k_pool/v_pool must be 16-byte and block_table/seq_lens 4-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  if (p->mode != PKV_MODE_UNSPLIT && !p->uploaded) {
+    set_error("plan has not been uploaded (pkv_plan_upload) since it was built");
+    return PKV_ERR_STATE;
+  }
+  const int G = p->group, D = s.head_dim;
+  PartialLaunch lp = pick_partial(s.dtype, G, D);
+  MergeLaunch lm = pick_merge(s.dtype, D);
+  if (!lp || !lm) {
+    set_error("no kernel for head_dim %d, G %d", D, G);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  char* ws = (char*)p->workspace;
+  const pkv_workspace_layout& L = p->layout;
+
+  PartialParams pp{};
+  pp.q = (const uint16_t*)q;
+  pp.k_pool = (const uint16_t*)k_pool;
+  pp.v_pool = (const uint16_t*)v_pool;
+  pp.block_table = block_table;
+  pp.seq_lens = seq_lens;
+  pp.out = (uint16_t*)out;
+  if (ws) {
+    pp.items = (const Item*)(ws + L.items_offset);
+    pp.ws_m = (float*)(ws + L.m_offset);
+    pp.ws_l = (float*)(ws + L.l_offset);
+    pp.ws_acc = (float*)(ws + L.acc_offset);
+  }
+  pp.num_pages = s.num_pages;
+  pp.stride = s.block_table_stride;
+  pp.num_kv_heads = s.num_kv_heads;
+  pp.num_q_heads = s.num_q_heads;
+  pp.mode = p->mode;
+  pp.num_splits = p->num_splits;
+  pp.scale_log2 = s.sm_scale * kLog2e;
+
+  hipError_t e;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  if (p->grid > 0) {
+    lp(dim3(p->grid), stream, pp);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail("partial kernel launch", e);
+  }
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  if (p->mode != PKV_MODE_UNSPLIT) {
+    MergeParams mp{};
+    mp.ws_m = pp.ws_m;
+    mp.ws_l = pp.ws_l;
+    mp.ws_acc = pp.ws_acc;
+    mp.meta = (const SeqMeta*)(ws + L.meta_offset);
+    mp.out = (uint16_t*)out;
+    mp.num_kv_heads = s.num_kv_heads;
+    mp.num_q_heads = s.num_q_heads;
+    mp.group = G;
+    mp.mode = p->mode;
+    mp.num_splits = p->num_splits;
+    lm(dim3(s.batch * s.num_q_heads), stream, mp);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail("merge kernel launch", e);
+  }
+  if (ev2 && (e = hipEventRecord(ev2, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status query_num_cus(int32_t* num_cus) {
+  int dev = 0, v = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || v <= 0) {
+    set_error("cannot query the device's compute-unit count (pass opts.num_cus): %s",
+              hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  *num_cus = v;
+  return PKV_OK;
+}
+
+void wait_upload(pkv_plan* p) {
+  if (p && p->upload_event) (void)hipEventSynchronize((hipEvent_t)p->upload_event);
+}
+
+void release_device_resources(pkv_plan* p) {
+  if (!p) return;
+  if (p->upload_event) {
+    (void)hipEventSynchronize((hipEvent_t)p->upload_event);
+    (void)hipEventDestroy((hipEvent_t)p->upload_event);
+    p->upload_event = nullptr;
+  }
+  if (p->pinned) {
+    (void)hipHostFree(p->pinned);
+    p->pinned = nullptr;
+    p->pinned_bytes = 0;
+  }
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+pkv_status pkv_plan_upload(pkv_plan* p, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  pkv::clear_error();
+  if (!p) {
+    pkv::set_error("plan is NULL");
+    return PKV_ERR_INVALID;
+  }
+  const size_t need = (size_t)p->layout.total_bytes;
+  if (need > 0) {
+    if (!workspace) {
+      pkv::set_error("workspace is NULL but the plan needs %zu bytes", need);
+      return PKV_ERR_WORKSPACE;
+    }
+    if (workspace_bytes < need) {
+      pkv::set_error("workspace of %zu bytes is smaller than the %zu the plan needs",
+                     workspace_bytes, need);
+      return PKV_ERR_WORKSPACE;
+    }
+    if ((uintptr_t)workspace % 256) {
+      pkv::set_error("workspace must be 256-byte aligned");
+      return PKV_ERR_WORKSPACE;
+    }
+  }
+  p->workspace = workspace;
+  p->workspace_bytes = workspace_bytes;
+  hipError_t e;
+  if (p->upload_bytes > 0) {
+    const size_t nb = (size_t)p->layout.meta_offset + p->meta.size() * sizeof(pkv::SeqMeta);
+    if (p->upload_event) (void)hipEventSynchronize((hipEvent_t)p->upload_event);
+    if (p->pinned_bytes < nb) {
+      if (p->pinned) (void)hipHostFree(p->pinned);
+      p->pinned = nullptr;
+      p->pinned_bytes = 0;
+      if ((e = hipHostMalloc(&p->pinned, nb, hipHostMallocDefault)) != hipSuccess)
+        return pkv::hip_fail("hipHostMalloc", e);
+      p->pinned_bytes = nb;
+    }
+    char* st = (char*)p->pinned;
+    std::memcpy(st + p->layout.items_offset, p->items.data(), p->items.size() * sizeof(pkv::Item));
+    std::memcpy(st + p->layout.meta_offset, p->meta.data(), p->meta.size() * sizeof(pkv::SeqMeta));
+    if ((e = hipMemcpyAsync(workspace, st, nb, hipMemcpyHostToDevice, stream)) != hipSuccess)
+      return pkv::hip_fail("hipMemcpyAsync", e);
+    if (!p->upload_event) {
+      hipEvent_t ev;
+      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess)
+        return pkv::hip_fail("hipEventCreate", e);
+      p->upload_event = ev;
+    }
+    if ((e = hipEventRecord((hipEvent_t)p->upload_event, stream)) != hipSuccess)
+      return pkv::hip_fail("hipEventRecord", e);
+  }
+  p->uploaded = true;
+  return PKV_OK;
+}
+
+pkv_status pkv_decode(const pkv_plan* p, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, void* out,
+                      hipStream_t stream) {
+  return pkv::decode_impl(p, q, k_pool, v_pool, block_table, seq_lens, out, stream, nullptr,
+                          nullptr, nullptr);
+}
+
+pkv_status pkv_decode_marked(const pkv_plan* p, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, hipStream_t stream,
+                             hipEvent_t before, hipEvent_t after_partial, hipEvent_t after_merge) {
+  return pkv::decode_impl(p, q, k_pool, v_pool, block_table, seq_lens, out, stream, before,
+                          after_partial, after_merge);
+}
+
+}  // extern "C"

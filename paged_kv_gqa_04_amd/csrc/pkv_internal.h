@@ -1,0 +1,91 @@
+// Internal declarations shared by the host planner (plan.cpp, HIP-free) and
+// the device side (decode.hip). Not part of the ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Tokens per KV page. The pages name 16-token blocks as the usual size
+// (LLM Primer ch. 8, section 8.1); the kernels are built for exactly that.
+constexpr int kPageTokens = 16;
+
+// Waves (64 lanes each) in one partial-kernel workgroup. A workgroup owns
+// one (sequence, KV head, page range) item; its waves take the range's
+// pages round-robin and merge their states in LDS at the end.
+constexpr int kWavesPerGroup = 4;
+
+// Work-queue item as the partial kernel reads it (16 bytes).
+struct Item {
+  int32_t bg;          // b * Hkv + g
+  int32_t page_begin;  // first page of the range (logical page index)
+  int32_t page_end;    // one past the last page
+  int32_t slot;        // partial-state slot this range writes
+};
+
+struct SeqMeta {
+  int32_t slot_base;  // first slot of sequence b
+  int32_t splits;     // S_b: ranges per KV head of sequence b
+};
+
+}  // namespace pkv
+
+struct pkv_plan {
+  pkv_shape shape{};
+  pkv_opts opts{};
+  int32_t group = 0;       // G
+  int32_t num_cus = 0;
+
+  // Resolved schedule.
+  int32_t mode = PKV_MODE_UNSPLIT;
+  int32_t num_splits = 1;  // S
+  int32_t chunk_pages = 0;
+  int32_t grid = 0;
+  int32_t num_items = 0;
+  int32_t empty_items = 0;
+  int32_t num_slots = 0;
+  int32_t bucket_launches = 0;
+  int64_t kv_tokens = 0;
+  int64_t algorithmic_bytes = 0;
+  int64_t partial_bytes = 0;
+  int64_t upload_bytes = 0;
+
+  std::vector<int32_t> seq_lens;
+  std::vector<pkv::Item> items;
+  std::vector<pkv::SeqMeta> meta;
+
+  pkv_workspace_layout layout{};
+
+  // Device binding (decode.hip owns these).
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+  bool uploaded = false;
+  void* pinned = nullptr;  // pinned staging of [items | meta]
+  size_t pinned_bytes = 0;
+  void* upload_event = nullptr;  // hipEvent_t of the last upload copy
+  int device = -1;
+};
+
+namespace pkv {
+
+// Thread-local error text (plan.cpp).
+void set_error(const char* fmt, ...);
+void clear_error();
+
+// Device-side hooks implemented in decode.hip.
+pkv_status query_num_cus(int32_t* num_cus);
+void wait_upload(pkv_plan* plan);           // block until staging is free
+void release_device_resources(pkv_plan* plan);
+
+// Shapes the kernels are instantiated for (decode.hip dispatches exactly
+// these): head_dim 64 or 128, G in {1, 2, 4, 8}.
+inline bool kernel_supported(int32_t head_dim, int32_t group) {
+  return (head_dim == 64 || head_dim == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+}  // namespace pkv

@@ -1,0 +1,425 @@
+// Host planner for one paged GQA decode step: policy, row-local page ranges,
+// compact work queue, workspace layout and scheduler counters.
+//
+// Integer work only, and no HIP calls (except asking the device for its CU
+// count when the caller does not supply one), so it runs and is tested on a
+// machine without a GPU.
+//
+// Method (PersistentKV explainer, Technical summary > Methodology):
+//  * sequence splitting: the token axis of each (sequence, KV head) is cut
+//    into disjoint ranges, each producing a partial online-softmax state that
+//    a merge kernel combines exactly (Methodology 1);
+//  * row-local bounds: range counts and boundaries come from each row's true
+//    length, not a padded one; a split with no tokens produces the neutral
+//    state and reads nothing (Methodology 1);
+//  * compact work queue: a 1-D grid over the non-empty
+//    (row, KV head, range) items only, so a ragged batch costs one partial
+//    and one merge launch instead of launches per distinct length
+//    (Methodology 1; Results, launch fan-out);
+//  * a calibrated policy chooses the path from the batch size and the
+//    lengths (Methodology 2). The pages' thresholds were fitted to a 28-SM
+//    consumer GPU; the rule here is stated in terms of the MI355X's compute
+//    units and workgroup residency instead.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <set>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+thread_local std::string g_error;
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// --- Policy constants (MI355X) -------------------------------------------
+// Items the partial kernel should expose per compute unit before splitting
+// stops paying: enough resident workgroups that every CU keeps several
+// pages of K/V in flight.
+constexpr int kTargetItemsPerCU = 2;
+// Smallest range worth a workgroup (pages): one page per wave at least two
+// times over, so each wave pipelines loads behind compute.
+constexpr int kMinChunkPages = 2 * kWavesPerGroup;
+
+int32_t pages_of(int32_t n) { return (int32_t)ceil_div(n, kPageTokens); }
+
+// Chunk (pages per range) that brings the item count near the target.
+int32_t auto_chunk(const pkv_plan& p, int64_t total_pages) {
+  int64_t target = (int64_t)p.num_cus * kTargetItemsPerCU;
+  int64_t work = total_pages * p.shape.num_kv_heads;
+  int64_t c = std::max<int64_t>(kMinChunkPages, ceil_div(work, std::max<int64_t>(1, target)));
+  c = align_up(c, kWavesPerGroup);
+  return (int32_t)std::min<int64_t>(c, INT32_MAX / 2);
+}
+
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+pkv_status validate(const pkv_shape* s, const int32_t* lens) {
+  if (!s) {
+    set_error("shape is NULL");
+    return PKV_ERR_INVALID;
+  }
+  if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 ||
+      s->head_dim <= 0 || s->page_size <= 0 || s->block_table_stride < 0 ||
+      s->num_pages < 0) {
+    set_error("shape has a negative or zero size");
+    return PKV_ERR_INVALID;
+  }
+  if (s->num_q_heads % s->num_kv_heads != 0) {
+    set_error("num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+              s->num_q_heads, s->num_kv_heads);
+    return PKV_ERR_INVALID;
+  }
+  if (!(s->sm_scale >= 0.0f) || std::isinf(s->sm_scale)) {
+    set_error("sm_scale must be finite and >= 0");
+    return PKV_ERR_INVALID;
+  }
+  if (s->dtype != PKV_F16 && s->dtype != PKV_BF16) {
+    set_error("unsupported dtype %d", s->dtype);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (s->page_size != kPageTokens) {
+    set_error("page_size %d unsupported (built for %d)", s->page_size, kPageTokens);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  int32_t G = s->num_q_heads / s->num_kv_heads;
+  if (!kernel_supported(s->head_dim, G)) {
+    set_error("no kernel for head_dim %d with G = %d", s->head_dim, G);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)s->batch * s->num_q_heads > INT32_MAX / 2) {
+    set_error("batch * num_q_heads too large");
+    return PKV_ERR_INVALID;
+  }
+  if (s->batch > 0 && !lens) {
+    set_error("seq_lens_host is NULL");
+    return PKV_ERR_INVALID;
+  }
+  const int64_t cap = (int64_t)s->block_table_stride * s->page_size;
+  for (int32_t b = 0; b < s->batch; ++b) {
+    if (lens[b] < 0 || lens[b] > cap) {
+      set_error("seq_lens[%d] = %d outside [0, %lld]", b, lens[b], (long long)cap);
+      return PKV_ERR_INVALID;
+    }
+    if (lens[b] > 0 && s->num_pages <= 0) {
+      set_error("num_pages is 0 but seq_lens[%d] = %d", b, lens[b]);
+      return PKV_ERR_INVALID;
+    }
+  }
+  return PKV_OK;
+}
+
+// Build the schedule for p.seq_lens under p.opts.
+pkv_status build(pkv_plan& p) {
+  const pkv_shape& s = p.shape;
+  const int32_t B = s.batch, Hkv = s.num_kv_heads, G = p.group, d = s.head_dim;
+
+  int64_t total_pages = 0, kv_tokens = 0;
+  int32_t max_pages = 0, active = 0;
+  std::set<int32_t> distinct;
+  bool same_len = true;
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t n = p.seq_lens[b];
+    total_pages += pages_of(n);
+    kv_tokens += n;
+    max_pages = std::max(max_pages, pages_of(n));
+    if (n > 0) {
+      ++active;
+      distinct.insert(n);
+    }
+    if (pages_of(n) != pages_of(p.seq_lens[0])) same_len = false;
+  }
+
+  // ---- mode ----
+  int32_t mode = p.opts.mode;
+  if (mode < PKV_MODE_AUTO || mode > PKV_MODE_WORKQUEUE) {
+    set_error("unknown mode %d", mode);
+    return PKV_ERR_INVALID;
+  }
+  if (p.opts.num_splits < 0 || p.opts.chunk_pages < 0) {
+    set_error("num_splits and chunk_pages must be >= 0");
+    return PKV_ERR_INVALID;
+  }
+  const int64_t target = (int64_t)p.num_cus * kTargetItemsPerCU;
+  int32_t chunk = p.opts.chunk_pages > 0 ? p.opts.chunk_pages : auto_chunk(p, total_pages);
+  if (mode == PKV_MODE_AUTO) {
+    const int64_t units = (int64_t)active * Hkv;
+    if (units == 0 || units >= target || max_pages <= chunk) {
+      mode = PKV_MODE_UNSPLIT;  // enough rows, or nothing worth splitting
+    } else if (same_len) {
+      mode = PKV_MODE_SPLIT;  // equal rows: the rectangular grid wastes nothing
+    } else {
+      mode = PKV_MODE_WORKQUEUE;
+    }
+  }
+
+  p.items.clear();
+  p.meta.clear();
+  p.mode = mode;
+  p.kv_tokens = kv_tokens;
+  p.bucket_launches = 2 * (int32_t)distinct.size();
+
+  int64_t num_slots = 0;
+  if (mode == PKV_MODE_UNSPLIT) {
+    p.num_splits = 1;
+    p.chunk_pages = max_pages;
+    p.grid = B * Hkv;
+    p.num_items = active * Hkv;
+    p.empty_items = p.grid - p.num_items;
+  } else if (mode == PKV_MODE_SPLIT) {
+    int32_t S = p.opts.num_splits > 0
+                    ? p.opts.num_splits
+                    : (int32_t)std::max<int64_t>(1, ceil_div(max_pages, chunk));
+    if (max_pages > 0) S = std::min(S, max_pages);
+    S = std::max(S, 1);
+    int64_t grid = (int64_t)B * Hkv * S;
+    if (grid > INT32_MAX / 2) {
+      set_error("split grid too large");
+      return PKV_ERR_INVALID;
+    }
+    int32_t items = 0, cmax = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      int32_t pg = pages_of(p.seq_lens[b]);
+      if (pg == 0) continue;
+      int32_t cb = (int32_t)ceil_div(pg, S);
+      cmax = std::max(cmax, cb);
+      items += (int32_t)ceil_div(pg, cb) * Hkv;
+    }
+    p.num_splits = S;
+    p.chunk_pages = cmax;
+    p.grid = (int32_t)grid;
+    p.num_items = items;
+    p.empty_items = p.grid - items;
+    num_slots = grid;
+  } else {  // WORKQUEUE
+    if (chunk <= 0) chunk = kMinChunkPages;
+    int32_t smax = 0;
+    p.meta.resize(B);
+    for (int32_t b = 0; b < B; ++b) {
+      int32_t pg = pages_of(p.seq_lens[b]);
+      int32_t Sb = (int32_t)ceil_div(pg, chunk);
+      p.meta[b] = {(int32_t)num_slots, Sb};
+      for (int32_t g = 0; g < Hkv; ++g)
+        for (int32_t si = 0; si < Sb; ++si)
+          p.items.push_back({b * Hkv + g, si * chunk, std::min(pg, (si + 1) * chunk),
+                             (int32_t)(num_slots + (int64_t)g * Sb + si)});
+      num_slots += (int64_t)Hkv * Sb;
+      smax = std::max(smax, Sb);
+      if (num_slots > INT32_MAX / 2) {
+        set_error("work queue too large");
+        return PKV_ERR_INVALID;
+      }
+    }
+    if (p.opts.queue_seed == 0) {
+      // Longest ranges first: the hardware hands workgroups out in launch
+      // order, so this is greedy longest-processing-time scheduling.
+      std::stable_sort(p.items.begin(), p.items.end(), [](const Item& a, const Item& b) {
+        return (a.page_end - a.page_begin) > (b.page_end - b.page_begin);
+      });
+    } else {
+      uint64_t st = p.opts.queue_seed;
+      for (size_t i = p.items.size(); i > 1; --i)
+        std::swap(p.items[i - 1], p.items[splitmix64(st) % i]);
+    }
+    p.num_splits = smax;
+    p.chunk_pages = chunk;
+    p.grid = (int32_t)p.items.size();
+    p.num_items = p.grid;
+    p.empty_items = 0;
+  }
+  p.num_slots = (int32_t)num_slots;
+
+  // ---- workspace layout ----
+  pkv_workspace_layout& L = p.layout;
+  L = pkv_workspace_layout{};
+  int64_t off = 0;
+  L.items_offset = off;
+  off = align_up(off + (int64_t)p.items.size() * (int64_t)sizeof(Item), kAlign);
+  L.meta_offset = off;
+  off = align_up(off + (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta), kAlign);
+  L.m_offset = off;
+  off = align_up(off + num_slots * G * 4, kAlign);
+  L.l_offset = off;
+  off = align_up(off + num_slots * G * 4, kAlign);
+  L.acc_offset = off;
+  off = align_up(off + num_slots * G * d * 4, kAlign);
+  L.total_bytes = (mode == PKV_MODE_UNSPLIT) ? 0 : off;
+  L.num_items = (int32_t)p.items.size();
+  L.num_slots = p.num_slots;
+  L.group = G;
+  L.num_splits = p.num_splits;
+
+  // ---- counters ----
+  const int64_t e = 2;  // fp16 / bf16
+  p.algorithmic_bytes = kv_tokens * Hkv * d * 2 * e + 2 * (int64_t)B * s.num_q_heads * d * e +
+                        total_pages * 4 + (int64_t)B * 4;
+  p.partial_bytes = 2 * num_slots * G * (int64_t)(d + 2) * 4;
+  p.upload_bytes = (mode == PKV_MODE_WORKQUEUE)
+                       ? (int64_t)p.items.size() * (int64_t)sizeof(Item) +
+                             (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta)
+                       : 0;
+  p.uploaded = false;
+  return PKV_OK;
+}
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+}
+
+void clear_error() { g_error.clear(); }
+
+}  // namespace pkv
+
+extern "C" {
+
+pkv_status pkv_plan_create(const pkv_shape* shape, const int32_t* seq_lens_host,
+                           const pkv_opts* opts, pkv_plan** out_plan) {
+  pkv::clear_error();
+  if (!out_plan) {
+    pkv::set_error("out_plan is NULL");
+    return PKV_ERR_INVALID;
+  }
+  *out_plan = nullptr;
+  pkv_status st = pkv::validate(shape, seq_lens_host);
+  if (st != PKV_OK) return st;
+  pkv_plan* p = new (std::nothrow) pkv_plan();
+  if (!p) {
+    pkv::set_error("out of host memory");
+    return PKV_ERR_INVALID;
+  }
+  p->shape = *shape;
+  if (p->shape.sm_scale == 0.0f) p->shape.sm_scale = 1.0f / std::sqrt((float)shape->head_dim);
+  if (opts) p->opts = *opts;
+  p->group = shape->num_q_heads / shape->num_kv_heads;
+  p->num_cus = p->opts.num_cus;
+  if (p->num_cus <= 0) {
+    st = pkv::query_num_cus(&p->num_cus);
+    if (st != PKV_OK) {
+      delete p;
+      return st;
+    }
+  }
+  p->seq_lens.assign(seq_lens_host, seq_lens_host + shape->batch);
+  st = pkv::build(*p);
+  if (st != PKV_OK) {
+    delete p;
+    return st;
+  }
+  *out_plan = p;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_update(pkv_plan* p, const int32_t* seq_lens_host) {
+  pkv::clear_error();
+  if (!p) {
+    pkv::set_error("plan is NULL");
+    return PKV_ERR_INVALID;
+  }
+  pkv_status st = pkv::validate(&p->shape, seq_lens_host);
+  if (st != PKV_OK) return st;
+  pkv::wait_upload(p);
+  p->seq_lens.assign(seq_lens_host, seq_lens_host + p->shape.batch);
+  return pkv::build(*p);
+}
+
+size_t pkv_plan_workspace_bytes(const pkv_plan* p) {
+  return p ? (size_t)p->layout.total_bytes : 0;
+}
+
+pkv_status pkv_plan_stats_get(const pkv_plan* p, pkv_plan_stats* s) {
+  pkv::clear_error();
+  if (!p || !s) {
+    pkv::set_error("plan or stats is NULL");
+    return PKV_ERR_INVALID;
+  }
+  *s = pkv_plan_stats{};
+  s->mode = p->mode;
+  s->num_splits = p->num_splits;
+  s->chunk_pages = p->chunk_pages;
+  s->grid = p->grid;
+  s->num_items = p->num_items;
+  s->empty_items = p->empty_items;
+  s->num_slots = p->num_slots;
+  s->launches = p->mode == PKV_MODE_UNSPLIT ? 1 : 2;
+  s->bucket_launches = p->bucket_launches;
+  s->kv_tokens = p->kv_tokens;
+  s->algorithmic_bytes = p->algorithmic_bytes;
+  s->partial_bytes = p->partial_bytes;
+  s->upload_bytes = p->upload_bytes;
+  s->workspace_bytes = p->layout.total_bytes;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_layout_get(const pkv_plan* p, pkv_workspace_layout* l) {
+  pkv::clear_error();
+  if (!p || !l) {
+    pkv::set_error("plan or layout is NULL");
+    return PKV_ERR_INVALID;
+  }
+  *l = p->layout;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_queue_get(const pkv_plan* p, void* dst, size_t bytes) {
+  pkv::clear_error();
+  if (!p) {
+    pkv::set_error("plan is NULL");
+    return PKV_ERR_INVALID;
+  }
+  const size_t need = (size_t)p->layout.meta_offset + p->meta.size() * sizeof(pkv::SeqMeta);
+  if (p->meta.empty() && p->items.empty()) return PKV_OK;
+  if (!dst || bytes < need) {
+    pkv::set_error("queue image needs %zu bytes", need);
+    return PKV_ERR_INVALID;
+  }
+  char* d = (char*)dst;
+  std::memset(d, 0, need);
+  std::memcpy(d + p->layout.items_offset, p->items.data(), p->items.size() * sizeof(pkv::Item));
+  std::memcpy(d + p->layout.meta_offset, p->meta.data(), p->meta.size() * sizeof(pkv::SeqMeta));
+  return PKV_OK;
+}
+
+void pkv_plan_destroy(pkv_plan* p) {
+  if (!p) return;
+  pkv::release_device_resources(p);
+  delete p;
+}
+
+const char* pkv_status_string(int32_t st) {
+  switch (st) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID: return "PKV_ERR_INVALID";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_STATE: return "PKV_ERR_STATE";
+    default: return "PKV_ERR_UNKNOWN";
+  }
+}
+
+const char* pkv_last_error(void) { return pkv::g_error.c_str(); }
+
+int32_t pkv_version(void) { return 100; }
+
+}  // extern "C"
