@@ -94,13 +94,13 @@ def partial_kernel_bytes(stats, spec, batch):
     return b + (out_bytes if stats["mode_name"] == "unsplit" else 0)
 
 
-def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev):
+def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, merge="fused"):
     import torch
     B = len(dev["seq_lens_host"])
     shape = P.make_shape(B, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                          dev["block_table_host"].shape[1], dev["num_pages"], spec.dtype,
                          dev["sm_scale"])
-    plan = P.Plan(shape, dev["seq_lens_host"], P.make_opts(mode, splits, chunk))
+    plan = P.Plan(shape, dev["seq_lens_host"], P.make_opts(mode, splits, chunk, merge=merge))
     plan.upload()
     stats = plan.stats()
     out = torch.empty_like(dev["q"])
@@ -171,6 +171,7 @@ def main():
     ap.add_argument("--mode", default=None)
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--merge", default="fused", choices=["fused", "kernel"])
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
@@ -204,7 +205,7 @@ def main():
     dev["replicas"] = reps
     ev = HipEvents()
 
-    r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev)
+    r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev, a.merge)
     st = r["stats"]
     B = len(dev["seq_lens_host"])
     alg = st["algorithmic_bytes"]
@@ -231,7 +232,8 @@ def main():
             "head_dim": spec.head_dim, "page_size": 16,
             "kv_tokens": int(st["kv_tokens"]), "pool_pages": int(dev["num_pages"]),
             "mode": st["mode_name"], "num_splits": st["num_splits"],
-            "chunk_pages": st["chunk_pages"], "seed": seed, "pool_replicas": replicas,
+            "chunk_pages": st["chunk_pages"], "merge": a.merge, "seed": seed,
+            "pool_replicas": replicas,
         },
         "us_per_step": round(r["step_us"], 2),
         "us_per_step_p10_p90": [round(r["step_us_p10"], 2), round(r["step_us_p90"], 2)],
@@ -261,6 +263,7 @@ def main():
             "mode": sa["mode_name"], "num_splits": sa["num_splits"],
             "chunk_pages": sa["chunk_pages"], "grid": sa["grid"],
             "us_per_step": round(ra["step_us"], 2),
+            "partial_us": round(ra["partial_us"], 2),
             "gbps": round(sa["algorithmic_bytes"] / (ra["step_us"] * 1e-6) / 1e9, 1),
         }
     if not a.no_cpu and case is not None:

@@ -90,6 +90,15 @@ typedef enum pkv_mode {
   PKV_MODE_WORKQUEUE = 3
 } pkv_mode;
 
+/* How split states are merged (SPLIT and WORKQUEUE modes).
+ *   FUSED   the partial kernel's last-arriving workgroup of each
+ *           (sequence, KV head) merges that row's states and writes out:
+ *           one launch per step.
+ *   KERNEL  a separate merge kernel runs after the partial kernel: two
+ *           launches per step (the pages' design).
+ * Both merge the states in split-index order and give identical bits. */
+typedef enum pkv_merge { PKV_MERGE_FUSED = 0, PKV_MERGE_KERNEL = 1 } pkv_merge;
+
 /* Problem shape. Supported: page_size 16; head_dim 64 or 128;
  * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
 typedef struct pkv_shape {
@@ -112,7 +121,8 @@ typedef struct pkv_opts {
   int32_t num_cus;     /* compute units to plan for (0 = ask the device) */
   uint32_t queue_seed; /* 0: longest ranges first; else a seeded shuffle of
                           the queue (results do not depend on queue order) */
-  int32_t reserved[3];
+  int32_t merge;       /* pkv_merge */
+  int32_t reserved[2];
 } pkv_opts;
 
 /* Scheduler-derived counters of one planned step (PersistentKV explainer,
@@ -123,10 +133,13 @@ typedef struct pkv_plan_stats {
   int32_t chunk_pages;     /* pages per range (SPLIT: the largest row's) */
   int32_t grid;            /* partial-kernel workgroups launched */
   int32_t num_items;       /* launched workgroups that read KV */
-  int32_t empty_items;     /* launched workgroups that only write a neutral
-                              state (SPLIT cells past a row's end) */
+  int32_t empty_items;     /* launched workgroups that read no KV: SPLIT
+                              cells past a row's end (neutral state), or,
+                              with the fused merge, one zero-fill item per
+                              KV head of an empty row (WORKQUEUE, slot -1) */
   int32_t num_slots;       /* partial states written and merged */
-  int32_t launches;        /* kernel launches per step: 1 or 2 */
+  int32_t launches;        /* kernel launches per step: 1 (unsplit, or
+                              fused merge) or 2 (separate merge kernel) */
   int32_t bucket_launches; /* launches exact-length bucketing would issue:
                               one partial + one merge per distinct N_b > 0 */
   int32_t reserved;
@@ -136,7 +149,9 @@ typedef struct pkv_plan_stats {
   int64_t partial_bytes;     /* merge-state traffic: bytes of (m, l, acc)
                                 written by the partial kernel + read by the
                                 merge kernel */
-  int64_t upload_bytes;      /* host-to-device bytes per step (the queue) */
+  int64_t upload_bytes;      /* host-to-device bytes per step: the queue,
+                                the per-row table and the zeroed merge
+                                counters */
   int64_t workspace_bytes;   /* what pkv_plan_workspace_bytes returns */
 } pkv_plan_stats;
 
@@ -152,6 +167,8 @@ typedef struct pkv_plan_stats {
 typedef struct pkv_workspace_layout {
   int64_t items_offset;  /* int32x4 {b*Hkv+g, page_begin, page_end, slot} */
   int64_t meta_offset;   /* int32x2 per sequence (WORKQUEUE) */
+  int64_t counters_offset; /* int32 per (sequence, KV head): arrivals of the
+                              current step (fused merge); 0 between steps */
   int64_t m_offset;      /* fp32 [num_slots][G] */
   int64_t l_offset;      /* fp32 [num_slots][G] */
   int64_t acc_offset;    /* fp32 [num_slots][G][d] */
@@ -203,11 +220,12 @@ pkv_status pkv_plan_stats_get(const pkv_plan* plan, pkv_plan_stats* stats);
 pkv_status pkv_plan_layout_get(const pkv_plan* plan,
                                pkv_workspace_layout* layout);
 
-/* Copy the host image of what pkv_plan_upload sends: the work-queue items
- * (int32x4 {b*Hkv+g, page_begin, page_end, slot} at items_offset) and the
- * per-sequence (slot_base, S_b) pairs at meta_offset, laid out exactly as in
- * the workspace. `bytes` must be at least meta_offset + 8*batch (0 is fine
- * when the plan uploads nothing). For inspection and tests. */
+/* Copy the host image of what pkv_plan_upload sends (upload_bytes of
+ * pkv_plan_stats): the work-queue items (int32x4
+ * {b*Hkv+g, page_begin, page_end, slot} at items_offset), the per-sequence
+ * (slot_base, S_b) pairs at meta_offset and the zeroed merge counters at
+ * counters_offset, laid out exactly as in the workspace. `bytes` must be at
+ * least upload_bytes (0 is fine when the plan uploads nothing). */
 pkv_status pkv_plan_queue_get(const pkv_plan* plan, void* dst, size_t bytes);
 
 /* Run one decode step on `stream` (asynchronous).

@@ -12,6 +12,7 @@ from ._pkv import (  # noqa: F401
     DTYPES,
     LIB_PATH,
     MODE_NAMES,
+    MERGES,
     MODES,
     PKV_BF16,
     PKV_ERR_HIP,
@@ -20,6 +21,8 @@ from ._pkv import (  # noqa: F401
     PKV_ERR_UNSUPPORTED,
     PKV_ERR_WORKSPACE,
     PKV_F16,
+    PKV_MERGE_FUSED,
+    PKV_MERGE_KERNEL,
     PKV_MODE_AUTO,
     PKV_MODE_SPLIT,
     PKV_MODE_UNSPLIT,
@@ -100,7 +103,7 @@ class Plan:
 
 def decode_step(q, k_pool, v_pool, block_table, seq_lens, seq_lens_host, *,
                 num_pages=None, sm_scale=0.0, mode="auto", num_splits=0,
-                chunk_pages=0, queue_seed=0, out=None):
+                chunk_pages=0, queue_seed=0, merge="fused", out=None):
     """Plan, upload and run one decode step on torch tensors; returns
     ``(out, stats)``. ``q``: [B, Hq, d]; pools: [num_pages, Hkv, 16, d];
     ``block_table``: int32 [B, stride]; ``seq_lens``: int32 [B] (device) with
@@ -111,7 +114,7 @@ def decode_step(q, k_pool, v_pool, block_table, seq_lens, seq_lens_host, *,
     dt = "bf16" if q.dtype == torch.bfloat16 else "f16"
     shape = make_shape(B, Hq, Hkv, d, block_table.shape[1],
                        k_pool.shape[0] if num_pages is None else num_pages, dt, sm_scale)
-    opts = make_opts(mode, num_splits, chunk_pages, 0, queue_seed)
+    opts = make_opts(mode, num_splits, chunk_pages, 0, queue_seed, merge)
     if out is None:
         out = torch.empty_like(q)
     with Plan(shape, seq_lens_host, opts) as plan:

@@ -37,6 +37,10 @@ MODES = {"auto": PKV_MODE_AUTO, "unsplit": PKV_MODE_UNSPLIT,
 MODE_NAMES = {v: k for k, v in MODES.items()}
 DTYPES = {"f16": PKV_F16, "bf16": PKV_BF16}
 
+PKV_MERGE_FUSED = 0
+PKV_MERGE_KERNEL = 1
+MERGES = {"fused": PKV_MERGE_FUSED, "kernel": PKV_MERGE_KERNEL}
+
 
 class pkv_shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("num_q_heads", C.c_int32),
@@ -49,7 +53,8 @@ class pkv_shape(C.Structure):
 class pkv_opts(C.Structure):
     _fields_ = [("mode", C.c_int32), ("num_splits", C.c_int32),
                 ("chunk_pages", C.c_int32), ("num_cus", C.c_int32),
-                ("queue_seed", C.c_uint32), ("reserved", C.c_int32 * 3)]
+                ("queue_seed", C.c_uint32), ("merge", C.c_int32),
+                ("reserved", C.c_int32 * 2)]
 
 
 class pkv_plan_stats(C.Structure):
@@ -65,7 +70,7 @@ class pkv_plan_stats(C.Structure):
 
 class pkv_workspace_layout(C.Structure):
     _fields_ = [("items_offset", C.c_int64), ("meta_offset", C.c_int64),
-                ("m_offset", C.c_int64), ("l_offset", C.c_int64),
+                ("counters_offset", C.c_int64), ("m_offset", C.c_int64), ("l_offset", C.c_int64),
                 ("acc_offset", C.c_int64), ("total_bytes", C.c_int64),
                 ("num_items", C.c_int32), ("num_slots", C.c_int32),
                 ("group", C.c_int32), ("num_splits", C.c_int32)]
@@ -138,10 +143,11 @@ def make_shape(batch, num_q_heads, num_kv_heads, head_dim, block_table_stride,
 
 
 def make_opts(mode="auto", num_splits=0, chunk_pages=0, num_cus=0,
-              queue_seed=0) -> pkv_opts:
+              queue_seed=0, merge="fused") -> pkv_opts:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
+    mg = MERGES[merge] if isinstance(merge, str) else int(merge)
     return pkv_opts(m, int(num_splits), int(chunk_pages), int(num_cus),
-                    int(queue_seed) & 0xFFFFFFFF)
+                    int(queue_seed) & 0xFFFFFFFF, mg)
 
 
 def _lens(seq_lens_host):
@@ -190,16 +196,26 @@ def pkv_plan_layout_get(plan: int) -> dict:
     return _struct_dict(s)
 
 
-def pkv_plan_queue_get(plan: int, batch: int):
-    """Host image of the upload: (items int32 [n, 4], meta int32 [B, 2])."""
+def pkv_plan_queue_get(plan: int, batch: int, num_kv_heads: int | None = None):
+    """Host image of the upload: (items int32 [n, 4], meta int32 [B, 2],
+    counters int32 [B*Hkv] or empty)."""
     lay = pkv_plan_layout_get(plan)
-    need = lay["meta_offset"] + 8 * batch if lay["num_items"] or batch else 0
+    need = pkv_plan_stats_get(plan)["upload_bytes"]
     buf = np.zeros(max(need, 1), dtype=np.uint8)
     _check(LIB.pkv_plan_queue_get(plan, buf.ctypes.data, need), "pkv_plan_queue_get")
-    items = buf[lay["items_offset"]:lay["items_offset"] + 16 * lay["num_items"]]
-    meta = buf[lay["meta_offset"]:lay["meta_offset"] + 8 * batch] if need else buf[:0]
+    img = buf[:need]
+
+    def cut(off, nbytes):
+        return img[off:off + nbytes] if off + nbytes <= need else img[:0]
+
+    items = cut(lay["items_offset"], 16 * lay["num_items"])
+    has_meta = lay["counters_offset"] > lay["meta_offset"]  # sections are packed
+    meta = cut(lay["meta_offset"], 8 * batch) if has_meta else img[:0]
+    cnt = (cut(lay["counters_offset"], 4 * batch * num_kv_heads)
+           if num_kv_heads is not None else img[:0])
     return (items.view(np.int32).reshape(-1, 4).copy(),
-            meta.view(np.int32).reshape(-1, 2).copy())
+            meta.view(np.int32).reshape(-1, 2).copy(),
+            cnt.view(np.int32).copy())
 
 
 def pkv_decode(plan: int, q, k_pool, v_pool, block_table, seq_lens, out, stream=0) -> None:

@@ -41,6 +41,10 @@ constexpr float kTau = 8.0f;
 // (-inf) is 0 and never NaN; far below any real logit.
 constexpr float kNoMax = -1.0e30f;
 constexpr int kThreads = kWavesPerGroup * 64;
+// Block-table entries staged in LDS at a time by the partial kernel.
+constexpr int kBtChunk = 512;
+// s_waitcnt immediate for gfx9: vmcnt(0), expcnt(7), lgkmcnt(15).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // ---------------------------------------------------------------- helpers
 
@@ -81,6 +85,30 @@ __device__ __forceinline__ uint16_t pack1(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Partial states cross workgroups, and XCDs with separate L2 caches, when
+// the last workgroup of a row merges them inside the partial kernel; they
+// move with device-scope (agent) stores and loads, which bypass a stale L2.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One step of the exact merge of partial states: (M, L, A) <- (M, L, A)
+// combined with (m, l, a); a state with m = -inf is neutral.
+__device__ __forceinline__ void merge4(float& M, float& L, float4& A, float m, float l, float4 a) {
+  const float mn = fmaxf(M, m);
+  const float co = M == -INFINITY ? 0.0f : fast_exp2(M - mn);
+  const float cn = m == -INFINITY ? 0.0f : fast_exp2(m - mn);
+  L = L * co + l * cn;
+  A.x = A.x * co + a.x * cn;
+  A.y = A.y * co + a.y * cn;
+  A.z = A.z * co + a.z * cn;
+  A.w = A.w * co + a.w * cn;
+  M = mn;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -116,12 +144,15 @@ struct PartialParams {
   float* __restrict__ ws_m;
   float* __restrict__ ws_l;
   float* __restrict__ ws_acc;
+  int32_t* __restrict__ counters;    // one per (sequence, KV head)
+  const SeqMeta* __restrict__ meta;  // work queue: (slot_base, S_b) per row
   int64_t num_pages;
   int32_t stride;
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t mode;
   int32_t num_splits;
+  int32_t fused;     // last-arriving workgroup of a row merges its states
   float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -137,6 +168,117 @@ struct MergeParams {
   int32_t mode;
   int32_t num_splits;
 };
+
+// ------------------------------------------------------------ state merge
+//
+// Merge the `count` partial states of one (sequence, KV head) row, slots
+// base .. base+count-1, into the row's G x D outputs. Run by a whole
+// workgroup: thread t owns a 4-float column c of the G x D state and the
+// slots s = t / NC, t / NC + NSUB, ... (NSUB column groups side by side), so
+// one round of loads covers up to NSUB * kMergeBatch slots; the subsets are
+// then combined in subset order. The order of operations depends only on
+// the slot indices, never on timing, so the fused tail and the separate
+// merge kernel (both call this) produce the same bits.
+//
+// m and l of neighbouring rows share cache lines and are read with
+// device-scope loads; a row's acc block is whole 128-byte lines that no
+// other workgroup reads, so plain loads see the device-scope stores.
+constexpr int kMergeBatch = 8;
+
+template <int DT, int G, int D>
+__device__ void merge_row(const float* ws_m, const float* ws_l, const float* ws_acc, int base,
+                          int count, uint16_t* out_row) {
+  constexpr int NC = G * D / 4;       // float4 columns of one state
+  constexpr int NSUB = kThreads / NC;  // slot subsets merged side by side
+  static_assert(NSUB >= 1 && NSUB * NC == kThreads, "layout");
+  __shared__ float s_M[NSUB][G], s_L[NSUB][G];
+  __shared__ float4 s_A[NSUB][NC];
+  const int t = threadIdx.x;
+  const int c = t % NC, sub = t / NC;
+  const int h = (c * 4) / D;
+  float M = -INFINITY, L = 0.0f;
+  float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  int s = sub;
+  for (; s + (kMergeBatch - 1) * NSUB < count; s += kMergeBatch * NSUB) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    float4 av[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int64_t st = base + s + j * NSUB;
+      mv[j] = ld_agent(ws_m + st * G + h);
+      lv[j] = ld_agent(ws_l + st * G + h);
+      av[j] = *(const float4*)(ws_acc + st * (G * D) + c * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) merge4(M, L, A, mv[j], lv[j], av[j]);
+  }
+  for (; s < count; s += NSUB) {
+    const int64_t st = base + s;
+    merge4(M, L, A, ld_agent(ws_m + st * G + h), ld_agent(ws_l + st * G + h),
+           *(const float4*)(ws_acc + st * (G * D) + c * 4));
+  }
+  if constexpr (NSUB > 1) {
+    s_A[sub][c] = A;
+    if ((c * 4) % D == 0) {
+      s_M[sub][h] = M;
+      s_L[sub][h] = L;
+    }
+    __syncthreads();
+    if (sub == 0) {
+#pragma unroll
+      for (int u = 1; u < NSUB; ++u) merge4(M, L, A, s_M[u][h], s_L[u][h], s_A[u][c]);
+    }
+  }
+  if (sub == 0) {
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const uint32_t lo = pack1<DT>(A.x * inv) | ((uint32_t)pack1<DT>(A.y * inv) << 16);
+    const uint32_t hi = pack1<DT>(A.z * inv) | ((uint32_t)pack1<DT>(A.w * inv) << 16);
+    *(uint2*)(out_row + c * 4) = make_uint2(lo, hi);
+  }
+}
+
+// --------------------------------------------------- fused merge (tail)
+//
+// Called by every workgroup of (sequence b, KV head g) after it has written
+// its partial state. A per-row counter counts arrivals; the workgroup that
+// arrives last merges all of the row's states in split-index order (so the
+// result does not depend on which one it is) and resets the counter for the
+// next step. No workgroup ever waits for another.
+//
+// Visibility without cache-wide fences: every state store is device-scope
+// (written through to the point of coherence shared by all XCDs) and each
+// wave waits for its own stores to complete (vmcnt 0) before the barrier
+// that precedes the arrival increment; the last arriver reads the states
+// with device-scope loads issued after it has seen every other arrival. A
+// full agent-scope fence would instead write back and invalidate the whole
+// L2 of the XCD, stalling every other workgroup there.
+template <int DT, int G, int D>
+__device__ void finish_group(const PartialParams& a, int b, int g) {
+  __shared__ int s_last;
+  const int bg = b * a.num_kv_heads + g;
+  int base, count;
+  if (a.mode == PKV_MODE_WORKQUEUE) {
+    const SeqMeta sm = a.meta[b];
+    count = sm.splits;
+    base = sm.slot_base + g * count;
+  } else {
+    count = a.num_splits;
+    base = bg * count;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's state stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(a.counters + bg, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == count - 1;
+    if (last) __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  merge_row<DT, G, D>(a.ws_m, a.ws_l, a.ws_acc, base, count,
+                      a.out + ((int64_t)b * a.num_q_heads + g * G) * D);
+}
 
 // ---------------------------------------------------------- partial kernel
 //
@@ -176,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   __shared__ float s_acc[W][G * D];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hkv = a.num_kv_heads;
 
   // ---- which range this workgroup owns ----
@@ -214,16 +356,17 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     // Empty range: neutral state (or zeros for an empty row), read nothing.
     for (int e = threadIdx.x; e < G * D; e += kThreads) {
       const int h = e / D, dd = e - h * D;
-      if (a.mode == PKV_MODE_UNSPLIT) {
+      if (a.mode == PKV_MODE_UNSPLIT || slot < 0) {  // empty row: zeros
         a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] = 0;
       } else {
-        a.ws_acc[((int64_t)slot * G + h) * D + dd] = 0.0f;
+        st_agent(a.ws_acc + ((int64_t)slot * G + h) * D + dd, 0.0f);
         if (dd == 0) {
-          a.ws_m[(int64_t)slot * G + h] = -INFINITY;
-          a.ws_l[(int64_t)slot * G + h] = 0.0f;
+          st_agent(a.ws_m + (int64_t)slot * G + h, -INFINITY);
+          st_agent(a.ws_l + (int64_t)slot * G + h, 0.0f);
         }
       }
     }
+    if (a.mode != PKV_MODE_UNSPLIT && a.fused && slot >= 0) finish_group<DT, G, D>(a, b, g);
     return;
   }
 
@@ -254,28 +397,11 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
   }
 
-  // Pages of this wave: pb + wave + W*k, k in [0, cnt).
-  const int span = pe - pb;
-  const int cnt = span > wave ? (span - wave + W - 1) / W : 0;
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.stride + pb + wave;
-
-  // Block-table entries, 64 per vector load, read out with v_readlane.
-  auto bt_load = [&](int k0) -> int {
-    const int k = k0 + lane;
-    return k < cnt ? bt_row[(int64_t)k * W] : 0;
-  };
-  int bt_cur = bt_load(0);
-  int bt_nxt = cnt > 64 ? bt_load(64) : 0;
-  int bt_pos = 0, bt_base = 0;
-  auto next_phys = [&]() -> int {
-    if (bt_pos == 64) {
-      bt_cur = bt_nxt;
-      bt_base += 64;
-      bt_pos = 0;
-      bt_nxt = cnt > bt_base + 64 ? bt_load(bt_base + 64) : 0;
-    }
-    return __builtin_amdgcn_readlane(bt_cur, bt_pos++);
-  };
+  // Block-table entries of the range are staged in LDS, kBtChunk at a time,
+  // and read back with a broadcast LDS read: an in-loop vector load of the
+  // table would make the compiler drain every outstanding K/V prefetch.
+  __shared__ int32_t s_bt[kBtChunk];
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.stride;
 
   struct Page {
     u32x4 k[NKP][NKL];
@@ -283,23 +409,34 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     int ntok;  // valid tokens of the page (0 if its table entry is bad)
   };
 
+  int cb = pb;  // first page of the staged chunk
+  int cnt = 0;  // pages of the chunk this wave computes
+  // Issues exactly one page worth of load instructions, always: step k past
+  // the wave's last page (k >= cnt) re-reads one 16-byte word of the chunk's
+  // first page instead, so every pipeline step issues the same loads and the
+  // compiler can wait for the oldest ring slot only (vmcnt) instead of
+  // draining the whole ring. Those slots are never computed.
   auto load_page = [&](Page& r, int k) {
-    const int lp = pb + wave + W * k;
-    int phys = next_phys();
+    const bool real = k < cnt;  // wave-uniform
+    const int ks = real ? k : 0;
+    const int lp = cb + wave + W * ks;
+    int phys = __builtin_amdgcn_readfirstlane(s_bt[wave + W * ks]);
     const bool ok = (uint64_t)(uint32_t)phys < (uint64_t)a.num_pages;
     r.ntok = ok ? min(P, n - lp * P) : 0;
     phys = ok ? phys : 0;
     const int64_t tile = ((int64_t)phys * Hkv + g) * TILE;
     const uint16_t* kp = a.k_pool + tile;
     const uint16_t* vp = a.v_pool + tile;
+    const int on = real ? 1 : 0;  // lane offsets vanish for the filler loads
 #pragma unroll
     for (int pk = 0; pk < NKP; ++pk)
 #pragma unroll
       for (int j = 0; j < NKL; ++j)
-        r.k[pk][j] = *(const u32x4*)(kp + (pk * TPK + kt) * D + j * 8 * LPT + kc * 8);
+        r.k[pk][j] = __builtin_nontemporal_load(
+            (const u32x4*)(kp + on * ((pk * TPK + kt) * D + j * 8 * LPT + kc * 8)));
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
-      r.v[i] = *(const u32x4*)(vp + (i * TPI + vr) * D + vc * 8);
+      r.v[i] = __builtin_nontemporal_load((const u32x4*)(vp + on * ((i * TPI + vr) * D + vc * 8)));
   };
 
   float* sp = s_p[wave];
@@ -381,16 +518,30 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Software pipeline: the next page's loads are in flight while the
-  // current page is computed.
-  Page buf0, buf1;
-  if (cnt > 0) load_page(buf0, 0);
-  for (int k = 0; k < cnt; k += 2) {
-    if (k + 1 < cnt) load_page(buf1, k + 1);
-    compute_page(buf0);
-    if (k + 1 >= cnt) break;
-    if (k + 2 < cnt) load_page(buf0, k + 2);
-    compute_page(buf1);
+  // Software pipeline: a ring of NB page buffers keeps the loads of the next
+  // NB-1 pages in flight while the current page is computed (one wave per
+  // SIMD cannot hide HBM latency with fewer). Pages of the chunk
+  // [cb, cb + kBtChunk) go to wave w in the order cb + w, cb + w + W, ...
+  constexpr int NB = G >= 8 ? 3 : 4;
+  Page ring[NB];
+  for (; cb < pe; cb += kBtChunk) {
+    const int span = min(pe - cb, kBtChunk);
+    if (cb != pb) __syncthreads();  // every wave is done with the last chunk
+    for (int i = threadIdx.x; i < span; i += kThreads) s_bt[i] = bt_row[cb + i];
+    __syncthreads();
+    cnt = span > wave ? (span - wave + W - 1) / W : 0;
+    if (cnt == 0) continue;
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) load_page(ring[i], i);
+    for (int k = 0; k < cnt; k += NB) {
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        const int kk = k + r;
+        if (kk >= cnt) break;
+        load_page(ring[(r + NB - 1) % NB], kk + NB - 1);
+        compute_page(ring[r]);
+      }
+    }
   }
 
   // ---- combine the wave states, then the workgroup's waves ----
@@ -433,58 +584,36 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
       a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] =
           pack1<DT>(L > 0.0f ? A / L : 0.0f);
     } else {
-      a.ws_acc[((int64_t)slot * G + h) * D + dd] = A;
+      st_agent(a.ws_acc + ((int64_t)slot * G + h) * D + dd, A);
       if (dd == 0) {
-        a.ws_m[(int64_t)slot * G + h] = L > 0.0f ? M : -INFINITY;
-        a.ws_l[(int64_t)slot * G + h] = L;
+        st_agent(a.ws_m + (int64_t)slot * G + h, L > 0.0f ? M : -INFINITY);
+        st_agent(a.ws_l + (int64_t)slot * G + h, L);
       }
     }
   }
+  if (a.mode != PKV_MODE_UNSPLIT && a.fused) finish_group<DT, G, D>(a, b, g);
 }
 
 // ------------------------------------------------------------ merge kernel
 //
-// One wave per (sequence b, query head h). Reduces the row's S_b partial
-// states in split-index order, so the result does not depend on the order
-// in which the partial kernel ran its items.
-template <int DT, int D>
-__global__ __launch_bounds__(64) void merge_kernel(MergeParams a) {
-  constexpr int E = D / 64;  // output elements per lane
-  const int lane = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int b = bh / a.num_q_heads;
-  const int h = bh - b * a.num_q_heads;
-  const int G = a.group;
-  const int g = h / G, hh = h - g * G;
-  int Sb, base;
+// The separate merge launch: one workgroup per (sequence b, KV head g),
+// running the same merge_row as the fused tail.
+template <int DT, int G, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams a) {
+  const int bg = blockIdx.x;
+  const int b = bg / a.num_kv_heads;
+  const int g = bg - b * a.num_kv_heads;
+  int base, count;
   if (a.mode == PKV_MODE_WORKQUEUE) {
     const SeqMeta sm = a.meta[b];
-    Sb = sm.splits;
-    base = sm.slot_base + g * Sb;
+    count = sm.splits;
+    base = sm.slot_base + g * count;
   } else {
-    Sb = a.num_splits;
-    base = (b * a.num_kv_heads + g) * Sb;
+    count = a.num_splits;
+    base = bg * count;
   }
-  float M = -INFINITY;
-  for (int s = lane; s < Sb; s += 64) M = fmaxf(M, a.ws_m[(int64_t)(base + s) * G + hh]);
-  M = wave_max(M);
-  float L = 0.0f, A[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) A[e] = 0.0f;
-#pragma unroll 4
-  for (int s = 0; s < Sb; ++s) {
-    const int64_t st = (int64_t)(base + s) * G + hh;
-    const float m = a.ws_m[st];
-    const float sc = m == -INFINITY ? 0.0f : fast_exp2(m - M);
-    L = fmaf(sc, a.ws_l[st], L);
-    const float* src = a.ws_acc + st * D + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) A[e] = fmaf(sc, src[e], A[e]);
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  uint16_t* dst = a.out + ((int64_t)b * a.num_q_heads + h) * D + lane * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) dst[e] = pack1<DT>(A[e] * inv);
+  merge_row<DT, G, D>(a.ws_m, a.ws_l, a.ws_acc, base, count,
+                      a.out + ((int64_t)b * a.num_q_heads + g * G) * D);
 }
 
 // -------------------------------------------------------------- dispatch
@@ -497,9 +626,9 @@ void launch_partial(dim3 grid, hipStream_t s, const PartialParams& p) {
   hipLaunchKernelGGL((partial_kernel<DT, G, D>), grid, dim3(kThreads), 0, s, p);
 }
 
-template <int DT, int D>
+template <int DT, int G, int D>
 void launch_merge(dim3 grid, hipStream_t s, const MergeParams& p) {
-  hipLaunchKernelGGL((merge_kernel<DT, D>), grid, dim3(64), 0, s, p);
+  hipLaunchKernelGGL((merge_kernel<DT, G, D>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <int DT, int D>
@@ -518,9 +647,20 @@ PartialLaunch pick_partial(int dt, int G, int D) {
   return D == 128 ? pick_partial_g<PKV_F16, 128>(G) : pick_partial_g<PKV_F16, 64>(G);
 }
 
-MergeLaunch pick_merge(int dt, int D) {
-  if (dt == PKV_BF16) return D == 128 ? launch_merge<PKV_BF16, 128> : launch_merge<PKV_BF16, 64>;
-  return D == 128 ? launch_merge<PKV_F16, 128> : launch_merge<PKV_F16, 64>;
+template <int DT, int D>
+MergeLaunch pick_merge_g(int G) {
+  switch (G) {
+    case 1: return launch_merge<DT, 1, D>;
+    case 2: return launch_merge<DT, 2, D>;
+    case 4: return launch_merge<DT, 4, D>;
+    case 8: return launch_merge<DT, 8, D>;
+    default: return nullptr;
+  }
+}
+
+MergeLaunch pick_merge(int dt, int G, int D) {
+  if (dt == PKV_BF16) return D == 128 ? pick_merge_g<PKV_BF16, 128>(G) : pick_merge_g<PKV_BF16, 64>(G);
+  return D == 128 ? pick_merge_g<PKV_F16, 128>(G) : pick_merge_g<PKV_F16, 64>(G);
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -560,7 +700,7 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
   }
   const int G = p->group, D = s.head_dim;
   PartialLaunch lp = pick_partial(s.dtype, G, D);
-  MergeLaunch lm = pick_merge(s.dtype, D);
+  MergeLaunch lm = pick_merge(s.dtype, G, D);
   if (!lp || !lm) {
     set_error("no kernel for head_dim %d, G %d", D, G);
     return PKV_ERR_UNSUPPORTED;
@@ -577,10 +717,13 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
   pp.out = (uint16_t*)out;
   if (ws) {
     pp.items = (const Item*)(ws + L.items_offset);
+    pp.meta = (const SeqMeta*)(ws + L.meta_offset);
+    pp.counters = (int32_t*)(ws + L.counters_offset);
     pp.ws_m = (float*)(ws + L.m_offset);
     pp.ws_l = (float*)(ws + L.l_offset);
     pp.ws_acc = (float*)(ws + L.acc_offset);
   }
+  pp.fused = p->fused;
   pp.num_pages = s.num_pages;
   pp.stride = s.block_table_stride;
   pp.num_kv_heads = s.num_kv_heads;
@@ -596,7 +739,7 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail("partial kernel launch", e);
   }
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
-  if (p->mode != PKV_MODE_UNSPLIT) {
+  if (p->mode != PKV_MODE_UNSPLIT && !p->fused) {
     MergeParams mp{};
     mp.ws_m = pp.ws_m;
     mp.ws_l = pp.ws_l;
@@ -608,7 +751,7 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
     mp.group = G;
     mp.mode = p->mode;
     mp.num_splits = p->num_splits;
-    lm(dim3(s.batch * s.num_q_heads), stream, mp);
+    lm(dim3(s.batch * s.num_kv_heads), stream, mp);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail("merge kernel launch", e);
   }
   if (ev2 && (e = hipEventRecord(ev2, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
@@ -679,7 +822,7 @@ pkv_status pkv_plan_upload(pkv_plan* p, void* workspace, size_t workspace_bytes,
   p->workspace_bytes = workspace_bytes;
   hipError_t e;
   if (p->upload_bytes > 0) {
-    const size_t nb = (size_t)p->layout.meta_offset + p->meta.size() * sizeof(pkv::SeqMeta);
+    const size_t nb = (size_t)p->upload_bytes;
     if (p->upload_event) (void)hipEventSynchronize((hipEvent_t)p->upload_event);
     if (p->pinned_bytes < nb) {
       if (p->pinned) (void)hipHostFree(p->pinned);
@@ -690,8 +833,7 @@ pkv_status pkv_plan_upload(pkv_plan* p, void* workspace, size_t workspace_bytes,
       p->pinned_bytes = nb;
     }
     char* st = (char*)p->pinned;
-    std::memcpy(st + p->layout.items_offset, p->items.data(), p->items.size() * sizeof(pkv::Item));
-    std::memcpy(st + p->layout.meta_offset, p->meta.data(), p->meta.size() * sizeof(pkv::SeqMeta));
+    pkv::write_upload_image(*p, st);
     if ((e = hipMemcpyAsync(workspace, st, nb, hipMemcpyHostToDevice, stream)) != hipSuccess)
       return pkv::hip_fail("hipMemcpyAsync", e);
     if (!p->upload_event) {

@@ -39,6 +39,7 @@ struct pkv_plan {
   pkv_opts opts{};
   int32_t group = 0;       // G
   int32_t num_cus = 0;
+  int32_t fused = 1;       // merge inside the partial kernel
 
   // Resolved schedule.
   int32_t mode = PKV_MODE_UNSPLIT;
@@ -71,6 +72,10 @@ struct pkv_plan {
 };
 
 namespace pkv {
+
+// Fill `dst` (upload_bytes long) with the workspace image the upload sends:
+// items, per-row table, zeroed counters (plan.cpp).
+void write_upload_image(const pkv_plan& p, void* dst);
 
 // Thread-local error text (plan.cpp).
 void set_error(const char* fmt, ...);

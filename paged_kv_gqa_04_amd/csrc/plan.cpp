@@ -154,6 +154,11 @@ pkv_status build(pkv_plan& p) {
     set_error("num_splits and chunk_pages must be >= 0");
     return PKV_ERR_INVALID;
   }
+  if (p.opts.merge != PKV_MERGE_FUSED && p.opts.merge != PKV_MERGE_KERNEL) {
+    set_error("unknown merge %d", p.opts.merge);
+    return PKV_ERR_INVALID;
+  }
+  p.fused = p.opts.merge == PKV_MERGE_FUSED;
   const int64_t target = (int64_t)p.num_cus * kTargetItemsPerCU;
   int32_t chunk = p.opts.chunk_pages > 0 ? p.opts.chunk_pages : auto_chunk(p, total_pages);
   if (mode == PKV_MODE_AUTO) {
@@ -217,6 +222,11 @@ pkv_status build(pkv_plan& p) {
         for (int32_t si = 0; si < Sb; ++si)
           p.items.push_back({b * Hkv + g, si * chunk, std::min(pg, (si + 1) * chunk),
                              (int32_t)(num_slots + (int64_t)g * Sb + si)});
+      // An empty row has no range; with the merge fused into the partial
+      // kernel nothing else would write its (zero) output, so it gets one
+      // zero-fill item per KV head (slot -1, no pages).
+      if (Sb == 0 && p.fused)
+        for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1});
       num_slots += (int64_t)Hkv * Sb;
       smax = std::max(smax, Sb);
       if (num_slots > INT32_MAX / 2) {
@@ -235,11 +245,13 @@ pkv_status build(pkv_plan& p) {
       for (size_t i = p.items.size(); i > 1; --i)
         std::swap(p.items[i - 1], p.items[splitmix64(st) % i]);
     }
+    int32_t fills = 0;
+    for (const Item& it : p.items) fills += it.slot < 0;
     p.num_splits = smax;
     p.chunk_pages = chunk;
     p.grid = (int32_t)p.items.size();
-    p.num_items = p.grid;
-    p.empty_items = 0;
+    p.num_items = p.grid - fills;
+    p.empty_items = fills;
   }
   p.num_slots = (int32_t)num_slots;
 
@@ -251,6 +263,10 @@ pkv_status build(pkv_plan& p) {
   off = align_up(off + (int64_t)p.items.size() * (int64_t)sizeof(Item), kAlign);
   L.meta_offset = off;
   off = align_up(off + (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta), kAlign);
+  L.counters_offset = off;
+  const bool counters = mode != PKV_MODE_UNSPLIT && p.fused;
+  const int64_t counters_end = off + (counters ? (int64_t)B * Hkv * 4 : 0);
+  off = align_up(counters_end, kAlign);
   L.m_offset = off;
   off = align_up(off + num_slots * G * 4, kAlign);
   L.l_offset = off;
@@ -268,15 +284,30 @@ pkv_status build(pkv_plan& p) {
   p.algorithmic_bytes = kv_tokens * Hkv * d * 2 * e + 2 * (int64_t)B * s.num_q_heads * d * e +
                         total_pages * 4 + (int64_t)B * 4;
   p.partial_bytes = 2 * num_slots * G * (int64_t)(d + 2) * 4;
-  p.upload_bytes = (mode == PKV_MODE_WORKQUEUE)
-                       ? (int64_t)p.items.size() * (int64_t)sizeof(Item) +
-                             (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta)
-                       : 0;
+  // Upload image: [items | meta | zeroed counters]; nothing when no table
+  // or counter is used.
+  if (mode == PKV_MODE_UNSPLIT)
+    p.upload_bytes = 0;
+  else if (counters)
+    p.upload_bytes = counters_end;
+  else if (mode == PKV_MODE_WORKQUEUE)
+    p.upload_bytes = L.meta_offset + (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta);
+  else
+    p.upload_bytes = 0;
   p.uploaded = false;
   return PKV_OK;
 }
 
 }  // namespace
+
+void write_upload_image(const pkv_plan& p, void* dst) {
+  char* d = (char*)dst;
+  std::memset(d, 0, (size_t)p.upload_bytes);
+  if (!p.items.empty())
+    std::memcpy(d + p.layout.items_offset, p.items.data(), p.items.size() * sizeof(Item));
+  if (!p.meta.empty())
+    std::memcpy(d + p.layout.meta_offset, p.meta.data(), p.meta.size() * sizeof(SeqMeta));
+}
 
 void set_error(const char* fmt, ...) {
   char buf[512];
@@ -361,7 +392,7 @@ pkv_status pkv_plan_stats_get(const pkv_plan* p, pkv_plan_stats* s) {
   s->num_items = p->num_items;
   s->empty_items = p->empty_items;
   s->num_slots = p->num_slots;
-  s->launches = p->mode == PKV_MODE_UNSPLIT ? 1 : 2;
+  s->launches = (p->mode == PKV_MODE_UNSPLIT || p->fused) ? 1 : 2;
   s->bucket_launches = p->bucket_launches;
   s->kv_tokens = p->kv_tokens;
   s->algorithmic_bytes = p->algorithmic_bytes;
@@ -387,16 +418,13 @@ pkv_status pkv_plan_queue_get(const pkv_plan* p, void* dst, size_t bytes) {
     pkv::set_error("plan is NULL");
     return PKV_ERR_INVALID;
   }
-  const size_t need = (size_t)p->layout.meta_offset + p->meta.size() * sizeof(pkv::SeqMeta);
-  if (p->meta.empty() && p->items.empty()) return PKV_OK;
+  const size_t need = (size_t)p->upload_bytes;
+  if (need == 0) return PKV_OK;
   if (!dst || bytes < need) {
     pkv::set_error("queue image needs %zu bytes", need);
     return PKV_ERR_INVALID;
   }
-  char* d = (char*)dst;
-  std::memset(d, 0, need);
-  std::memcpy(d + p->layout.items_offset, p->items.data(), p->items.size() * sizeof(pkv::Item));
-  std::memcpy(d + p->layout.meta_offset, p->meta.data(), p->meta.size() * sizeof(pkv::SeqMeta));
+  pkv::write_upload_image(*p, dst);
   return PKV_OK;
 }
 

@@ -44,7 +44,7 @@ def shape_of(case, num_pages=None):
 
 
 def run_case(case, dev=None, mode="auto", num_splits=0, chunk_pages=0, queue_seed=0,
-             return_plan=False):
+             return_plan=False, merge="fused"):
     """Decode ``case`` on the GPU; returns float64 out (and the Plan)."""
     import torch
 
@@ -53,7 +53,7 @@ def run_case(case, dev=None, mode="auto", num_splits=0, chunk_pages=0, queue_see
         dev = W.case_to_device(case)
     out = torch.full_like(dev["q"], float("nan"))
     plan = P.Plan(shape_of(case), case.seq_lens,
-                  P.make_opts(mode, num_splits, chunk_pages, 0, queue_seed))
+                  P.make_opts(mode, num_splits, chunk_pages, 0, queue_seed, merge))
     plan.upload()
     plan.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
                 dev["seq_lens"], out)

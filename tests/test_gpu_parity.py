@@ -230,6 +230,44 @@ def test_repeated_runs_bitwise():
         np.testing.assert_array_equal(bits, ref)
 
 
+# ------------------------------------------------------ merge placement
+
+
+@pytest.mark.parametrize("mode", ["split", "workqueue"])
+def test_fused_and_kernel_merge_give_identical_bits(mode):
+    c = _mini([3000, 17, 0, 900, 4100], seed=12)
+    kw = dict(mode=mode, num_splits=6 if mode == "split" else 0,
+              chunk_pages=5 if mode == "workqueue" else 0, return_plan=True)
+    _, pf, of = run_case(c, merge="fused", **kw)
+    _, pk, ok = run_case(c, merge="kernel", **kw)
+    assert pf.stats()["launches"] == 1 and pk.stats()["launches"] == 2
+    np.testing.assert_array_equal(out_bits(of), out_bits(ok))
+    assert_parity(of.to(torch.float64).cpu().numpy(), O.decode_case(c), f"fused/{mode}")
+    pf.close()
+    pk.close()
+
+
+@pytest.mark.parametrize("mode", ["split", "workqueue"])
+def test_fused_counters_reset_between_steps(mode):
+    """One upload, several decodes: each step's last workgroup resets the
+    per-row arrival counters, so later steps merge exactly as the first."""
+    c = _mini([2000, 33, 700], seed=13)
+    dev = W.case_to_device(c)
+    _, plan, out = run_case(c, dev, mode=mode, num_splits=4 if mode == "split" else 0,
+                            return_plan=True)
+    first = out_bits(out)
+    for _ in range(4):
+        out.fill_(float("nan"))
+        plan.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
+                    dev["seq_lens"], out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out_bits(out), first)
+    lay = plan.layout()
+    cnt = plan.workspace[lay["counters_offset"]:lay["counters_offset"] + 4 * c.batch * c.num_kv_heads]
+    assert (cnt.cpu().numpy().view(np.int32) == 0).all()
+    plan.close()
+
+
 # --------------------------------------------- partial states on their own
 
 

@@ -23,13 +23,13 @@ CUS = 256
 
 
 def plan(lens, mode="auto", S=0, chunk=0, Hq=32, Hkv=8, d=128, seed=0, stride=None,
-         num_pages=None, dtype="bf16", cus=CUS):
+         num_pages=None, dtype="bf16", cus=CUS, merge="fused"):
     lens = np.asarray(lens, dtype=np.int32)
     pages = [(int(n) + 15) // 16 for n in lens]
     stride = max(1, max(pages) if pages else 1) if stride is None else stride
     num_pages = max(1, sum(pages)) if num_pages is None else num_pages
     shape = P.make_shape(len(lens), Hq, Hkv, d, stride, num_pages, dtype)
-    return P.pkv_plan_create(shape, lens, P.make_opts(mode, S, chunk, cus, seed))
+    return P.pkv_plan_create(shape, lens, P.make_opts(mode, S, chunk, cus, seed, merge))
 
 
 def ranges_by_row(items, meta, lens, Hkv, mode, S=None, chunk=None):
@@ -82,14 +82,22 @@ def test_workqueue_partitions_rows_without_empty_items(lens, chunk):
     Hkv = 8
     h = plan(lens, "workqueue", chunk=chunk, Hkv=Hkv)
     st = P.pkv_plan_stats_get(h)
-    items, meta = P.pkv_plan_queue_get(h, len(lens))
+    items, meta, cnt = P.pkv_plan_queue_get(h, len(lens), Hkv)
     lay = P.pkv_plan_layout_get(h)
-    assert st["mode_name"] == "workqueue" and st["launches"] == 2
+    assert st["mode_name"] == "workqueue" and st["launches"] == 1  # fused merge
+    assert cnt.shape == (len(lens) * Hkv,) and (cnt == 0).all()
+    assert st["upload_bytes"] == lay["counters_offset"] + 4 * len(lens) * Hkv
     ck = st["chunk_pages"]
     assert chunk == 0 or ck == chunk
-    assert len(items) == st["num_items"] == st["grid"] == lay["num_items"]
-    assert st["empty_items"] == 0
-    assert (items[:, 2] > items[:, 1]).all()  # no empty items
+    assert len(items) == st["grid"] == lay["num_items"]
+    fill = items[:, 3] < 0  # zero-fill items of empty rows (fused merge only)
+    n_empty_rows = sum(1 for n in lens if n == 0)
+    assert fill.sum() == st["empty_items"] == n_empty_rows * Hkv
+    assert (items[fill, 1] == items[fill, 2]).all()
+    assert all(lens[bg // Hkv] == 0 for bg in items[fill, 0])
+    items = items[~fill]
+    assert len(items) == st["num_items"]
+    assert (items[:, 2] > items[:, 1]).all()  # no empty ranges in the queue
     slots = items[:, 3]
     assert len(set(slots.tolist())) == len(slots) == st["num_slots"]
     assert slots.min(initial=0) >= 0 and slots.max(initial=-1) < st["num_slots"]
@@ -115,11 +123,12 @@ def test_workqueue_partitions_rows_without_empty_items(lens, chunk):
 def test_workqueue_runs_longest_ranges_first_and_shuffles_on_request():
     lens = [256, 1000, 5000, 300, 17, 9000]
     h = plan(lens, "workqueue", chunk=16)
-    items, _ = P.pkv_plan_queue_get(h, len(lens))
+    items = P.pkv_plan_queue_get(h, len(lens))[0]
     lengths = items[:, 2] - items[:, 1]
+    assert (items[:, 3] >= 0).all()
     assert (np.diff(lengths) <= 0).all()
     h2 = plan(lens, "workqueue", chunk=16, seed=77)
-    items2, _ = P.pkv_plan_queue_get(h2, len(lens))
+    items2 = P.pkv_plan_queue_get(h2, len(lens))[0]
     assert not np.array_equal(items, items2)
     key = lambda a: sorted(map(tuple, a.tolist()))
     assert key(items) == key(items2)
@@ -142,8 +151,21 @@ def test_split_grid_counts(lens, S):
             cb = math.ceil(pages / S_eff)
             busy += Hkv * math.ceil(pages / cb)
     assert st["num_items"] == busy and st["empty_items"] == st["grid"] - busy
-    assert P.pkv_plan_queue_get(h, len(lens))[0].size == 0  # nothing uploaded
-    assert st["upload_bytes"] == 0
+    items, meta, cnt = P.pkv_plan_queue_get(h, len(lens), Hkv)
+    assert items.size == 0 and meta.size == 0  # no queue: cells find their range
+    assert (cnt == 0).all() and cnt.size == len(lens) * Hkv  # fused-merge counters
+    hk = plan(lens, "split", S=S, Hkv=Hkv, merge="kernel")
+    assert P.pkv_plan_stats_get(hk)["upload_bytes"] == 0
+    assert P.pkv_plan_stats_get(hk)["launches"] == 2
+
+
+def test_workqueue_separate_merge_has_no_fill_items():
+    lens = [0, 100, 0, 5]
+    h = plan(lens, "workqueue", chunk=2, merge="kernel")
+    st = P.pkv_plan_stats_get(h)
+    items = P.pkv_plan_queue_get(h, len(lens))[0]
+    assert st["empty_items"] == 0 and (items[:, 3] >= 0).all()
+    assert (items[:, 2] > items[:, 1]).all()
 
 
 def test_unsplit_counts():
@@ -175,9 +197,12 @@ def test_golden_launch_fanout_from_the_pages():
     long_ = rng.integers(12000, 20000, size=4)
     lens = np.concatenate([short, long_]).astype(np.int32)
     assert len(set(lens.tolist())) == g["batch"] == 8
-    st = P.pkv_plan_stats_get(plan(lens, "workqueue"))
+    # the pages' design: a separate merge kernel after the partial kernel
+    st = P.pkv_plan_stats_get(plan(lens, "workqueue", merge="kernel"))
     assert st["launches"] == g["work_queue_launches_per_step"]
     assert st["bucket_launches"] == g["exact_length_bucketing_launches_per_step"]
+    # the fused merge folds the second launch into the first
+    assert P.pkv_plan_stats_get(plan(lens, "workqueue"))["launches"] == 1
 
 
 # ------------------------------------------------------------------ policy
@@ -225,7 +250,7 @@ def test_plan_create_errors(kw, status):
 
 
 def test_negative_lengths_and_modes_rejected():
-    for lens, kw in [([-1], {}), ([5], dict(mode=9)), ([5], dict(S=-2))]:
+    for lens, kw in [([-1], {}), ([5], dict(mode=9)), ([5], dict(S=-2)), ([5], dict(merge=3))]:
         with pytest.raises(P.PkvError) as e:
             plan(lens, **kw)
         assert e.value.status == P.PKV_ERR_INVALID
