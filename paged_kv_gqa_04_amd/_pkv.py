@@ -15,7 +15,9 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# PKV_LIBRARY may name another build of the same ABI (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID = -1

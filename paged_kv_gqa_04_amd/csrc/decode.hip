@@ -29,6 +29,8 @@ namespace pkv {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define GPTR(p) ((__attribute__((address_space(1))) void*)(p))
+#define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
@@ -41,10 +43,19 @@ constexpr float kTau = 8.0f;
 // (-inf) is 0 and never NaN; far below any real logit.
 constexpr float kNoMax = -1.0e30f;
 constexpr int kThreads = kWavesPerGroup * 64;
+// K/V ring slots (pages in flight + 1) per wave of the partial kernel.
+#ifndef PKV_RING_SLOTS
+#define PKV_RING_SLOTS 2
+#endif
+constexpr int kRingSlots = PKV_RING_SLOTS;
 // Block-table entries staged in LDS at a time by the partial kernel.
 constexpr int kBtChunk = 512;
-// s_waitcnt immediate for gfx9: vmcnt(0), expcnt(7), lgkmcnt(15).
-constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate for gfx9: vmcnt(n) (6 bits: [3:0] and [15:14]) with
+// expcnt(7) and lgkmcnt(15), i.e. wait on vector-memory loads only.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kWaitVmcnt0 = waitcnt_vm(0);
+// Cache-policy operand of the direct-to-LDS load builtin: nontemporal.
+constexpr int kLoadNontemporal = 2;
 
 // ---------------------------------------------------------------- helpers
 
@@ -129,6 +140,53 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
+}
+
+// Read one ring slot back from LDS: wait until at most VM vector-memory
+// loads are outstanding (the slot's own direct-to-LDS loads have landed),
+// then read this lane's K pieces (at the per-lane LDS byte addresses ka[])
+// and V pieces (va, va + 1 KiB, ...), and wait for them.
+#define PKV_READ8(VMS)                                                                      \
+  asm volatile("s_waitcnt vmcnt(" VMS ")\n"                                                \
+               "ds_read_b128 %0, %8\n"                                                     \
+               "ds_read_b128 %1, %9\n"                                                     \
+               "ds_read_b128 %2, %10\n"                                                    \
+               "ds_read_b128 %3, %11\n"                                                    \
+               "ds_read_b128 %4, %12\n"                                                    \
+               "ds_read_b128 %5, %12 offset:1024\n"                                        \
+               "ds_read_b128 %6, %12 offset:2048\n"                                        \
+               "ds_read_b128 %7, %12 offset:3072\n"                                        \
+               "s_waitcnt lgkmcnt(0)"                                                       \
+               : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(kk[2]), "=&v"(kk[3]), "=&v"(v[0]),        \
+                 "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])                                      \
+               : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va)                    \
+               : "memory")
+#define PKV_READ4(VMS)                                                                      \
+  asm volatile("s_waitcnt vmcnt(" VMS ")\n"                                                \
+               "ds_read_b128 %0, %4\n"                                                     \
+               "ds_read_b128 %1, %5\n"                                                     \
+               "ds_read_b128 %2, %6\n"                                                     \
+               "ds_read_b128 %3, %6 offset:1024\n"                                         \
+               "s_waitcnt lgkmcnt(0)"                                                       \
+               : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(v[0]), "=&v"(v[1])                       \
+               : "v"(ka[0]), "v"(ka[1]), "v"(va)                                            \
+               : "memory")
+
+template <int LPP, int VM, typename KArr, typename VArr>
+__device__ __forceinline__ void read_slot(const uint32_t* ka, uint32_t va, KArr& k, VArr& v) {
+  u32x4* kk = &k[0][0];
+  if constexpr (LPP == 8) {
+    if constexpr (VM == 8) PKV_READ8("8");
+    else if constexpr (VM == 16) PKV_READ8("16");
+    else if constexpr (VM == 24) PKV_READ8("24");
+    else static_assert(VM == 8, "ring depth");
+  } else {
+    static_assert(LPP == 4, "loads per page");
+    if constexpr (VM == 4) PKV_READ4("4");
+    else if constexpr (VM == 8) PKV_READ4("8");
+    else if constexpr (VM == 12) PKV_READ4("12");
+    else static_assert(VM == 4, "ring depth");
+  }
 }
 
 // ------------------------------------------------------------- parameters
@@ -312,10 +370,26 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   constexpr int NVI = P / TPI;   // V loads per lane per page
   constexpr int TILE = P * D;    // elements of one (page, KV head) tile
 
+  constexpr int LPP = NKP * NKL + NVI;  // 16-byte load instructions per page
+  constexpr int NB = kRingSlots;        // ring slots per wave (pages)
+  constexpr int SLOT_WORDS = LPP * 256;  // one slot: LPP x 64 lanes x 16 B
+
+  // K/V ring: each wave owns NB slots, filled by direct-to-LDS loads. Lane i
+  // of a load instruction lands at (instruction base + 16 i) and is read back
+  // by lane i itself, so the ring needs no registers and no bank-friendly
+  // layout. The ring is reused for the cross-wave combine at the end.
+  // One LDS array per slot (not one array indexed by slot): the compiler
+  // then sees that reading slot r cannot alias the loads still landing in
+  // the other slots and waits for slot r's loads only.
+  static_assert(NB >= 2 && NB <= 4, "two to four slot arrays");
+  __shared__ __attribute__((aligned(16))) uint32_t s_ring0[W * SLOT_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_ring1[W * SLOT_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_ring2[NB > 2 ? W * SLOT_WORDS : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_ring3[NB > 3 ? W * SLOT_WORDS : 4];
   __shared__ float s_p[W][P * G];
   __shared__ float s_m[W][G];
   __shared__ float s_l[W][G];
-  __shared__ float s_acc[W][G * D];
+  static_assert(G * D <= SLOT_WORDS, "combine buffer fits in one ring array");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -373,18 +447,28 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   const int kt = lane / LPT, kc = lane % LPT;
   const int vr = lane / VL, vc = lane % VL;
 
-  // q of the group's G heads, in the K layout (packed pairs).
+  // K sits in its LDS slot exactly as in memory (token rows of D elements).
+  // Lane (kt, kc) takes, at step j, the 16*LPT-byte column block
+  // jr = (j + kt) % NKL of token kt: the rotation by token keeps the 16
+  // lanes of an LDS read phase on distinct banks. The dot product does not
+  // care about the order of d, so q is held in the same rotated order.
   uint32_t qr[G][EK / 2];
+  uint32_t kofs[NKP * NKL];  // this lane's K byte offsets inside a slot
   {
     const uint16_t* qb = a.q + ((int64_t)b * a.num_q_heads + g * G) * D;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int j = 0; j < NKL; ++j) {
+      const int jr = (j + kt) % NKL;
 #pragma unroll
-      for (int j = 0; j < NKL; ++j) {
-        const u32x4 v = *(const u32x4*)(qb + h * D + j * 8 * LPT + kc * 8);
+      for (int h = 0; h < G; ++h) {
+        const u32x4 v = *(const u32x4*)(qb + h * D + jr * 8 * LPT + kc * 8);
 #pragma unroll
         for (int w = 0; w < 4; ++w) qr[h][j * 4 + w] = v[w];
       }
+#pragma unroll
+      for (int pk = 0; pk < NKP; ++pk)
+        kofs[pk * NKL + j] = ((pk * TPK + kt) * D + jr * 8 * LPT + kc * 8) * 2;
+    }
   }
 
   float acc[G][8];
@@ -411,32 +495,54 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
 
   int cb = pb;  // first page of the staged chunk
   int cnt = 0;  // pages of the chunk this wave computes
-  // Issues exactly one page worth of load instructions, always: step k past
-  // the wave's last page (k >= cnt) re-reads one 16-byte word of the chunk's
-  // first page instead, so every pipeline step issues the same loads and the
-  // compiler can wait for the oldest ring slot only (vmcnt) instead of
-  // draining the whole ring. Those slots are never computed.
-  auto load_page = [&](Page& r, int k) {
+  int ntok_ring[NB];
+  auto slot_base = [&](int sl) -> uint32_t* {
+    uint32_t* base = sl == 0 ? s_ring0 : sl == 1 ? s_ring1 : sl == 2 ? s_ring2 : s_ring3;
+    return base + wave * SLOT_WORDS;
+  };
+
+  // Issue one page's LPP direct-to-LDS loads into ring slot `sl`. Always
+  // exactly LPP instructions: step k past the wave's last page (k >= cnt)
+  // re-reads one 16-byte word of the chunk's first page instead, so the
+  // number of loads in flight behind any slot is fixed and the wait before
+  // computing a slot is a constant vmcnt.
+  auto issue_page = [&](int sl, int k) {
     const bool real = k < cnt;  // wave-uniform
     const int ks = real ? k : 0;
     const int lp = cb + wave + W * ks;
     int phys = __builtin_amdgcn_readfirstlane(s_bt[wave + W * ks]);
     const bool ok = (uint64_t)(uint32_t)phys < (uint64_t)a.num_pages;
-    r.ntok = ok ? min(P, n - lp * P) : 0;
+    ntok_ring[sl] = ok ? min(P, n - lp * P) : 0;
     phys = ok ? phys : 0;
     const int64_t tile = ((int64_t)phys * Hkv + g) * TILE;
     const uint16_t* kp = a.k_pool + tile;
     const uint16_t* vp = a.v_pool + tile;
     const int on = real ? 1 : 0;  // lane offsets vanish for the filler loads
+    uint32_t* dst = slot_base(sl);
 #pragma unroll
-    for (int pk = 0; pk < NKP; ++pk)
-#pragma unroll
-      for (int j = 0; j < NKL; ++j)
-        r.k[pk][j] = __builtin_nontemporal_load(
-            (const u32x4*)(kp + on * ((pk * TPK + kt) * D + j * 8 * LPT + kc * 8)));
+    for (int i = 0; i < NKP * NKL; ++i)  // K: 1 KiB contiguous per instruction
+      __builtin_amdgcn_global_load_lds(GPTR(kp + on * (i * 512 + lane * 8)),
+                                       LPTR(dst + i * 256), 16, 0, kLoadNontemporal);
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
-      r.v[i] = __builtin_nontemporal_load((const u32x4*)(vp + on * ((i * TPI + vr) * D + vc * 8)));
+      __builtin_amdgcn_global_load_lds(GPTR(vp + on * ((i * TPI + vr) * D + vc * 8)),
+                                       LPTR(dst + (NKP * NKL + i) * 256), 16, 0,
+                                       kLoadNontemporal);
+  };
+
+  // Wait until slot `sl` has landed (the NB-1 younger pages may stay in
+  // flight), then read this lane's 16-byte pieces back. The wait and the LDS
+  // reads are one asm block: left to itself the compiler cannot tell the
+  // ring slots apart at the loop back-edge and drains every load in flight.
+  auto fetch_page = [&](int sl) -> Page {
+    Page r;
+    const uint32_t base = (uint32_t)(uintptr_t)LPTR(slot_base(sl));
+    uint32_t ka[NKP * NKL];
+#pragma unroll
+    for (int i = 0; i < NKP * NKL; ++i) ka[i] = base + kofs[i];
+    read_slot<LPP, (NB - 1) * LPP>(ka, base + (NKP * NKL) * 1024 + lane * 16, r.k, r.v);
+    r.ntok = ntok_ring[sl];
+    return r;
   };
 
   float* sp = s_p[wave];
@@ -518,12 +624,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Software pipeline: a ring of NB page buffers keeps the loads of the next
-  // NB-1 pages in flight while the current page is computed (one wave per
-  // SIMD cannot hide HBM latency with fewer). Pages of the chunk
+  // Software pipeline over the LDS ring: the loads of the next NB-1 pages
+  // are in flight while the current page is computed. Pages of the chunk
   // [cb, cb + kBtChunk) go to wave w in the order cb + w, cb + w + W, ...
-  constexpr int NB = G >= 8 ? 3 : 4;
-  Page ring[NB];
   for (; cb < pe; cb += kBtChunk) {
     const int span = min(pe - cb, kBtChunk);
     if (cb != pb) __syncthreads();  // every wave is done with the last chunk
@@ -532,16 +635,17 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     cnt = span > wave ? (span - wave + W - 1) / W : 0;
     if (cnt == 0) continue;
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i) load_page(ring[i], i);
+    for (int i = 0; i < NB - 1; ++i) issue_page(i, i);
     for (int k = 0; k < cnt; k += NB) {
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
         const int kk = k + r;
         if (kk >= cnt) break;
-        load_page(ring[(r + NB - 1) % NB], kk + NB - 1);
-        compute_page(ring[r]);
+        issue_page((r + NB - 1) % NB, kk + NB - 1);
+        compute_page(fetch_page(r));
       }
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // drain the filler loads
   }
 
   // ---- combine the wave states, then the workgroup's waves ----
@@ -554,6 +658,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
 #pragma unroll
       for (int m = VL; m < 64; m <<= 1) acc[h][e] += __shfl_xor(acc[h][e], m);
   }
+  float* s_acc = reinterpret_cast<float*>(s_ring0);  // [W][G * D], ring is done
+  __syncthreads();
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -565,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave][h * D + lane * 8 + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) s_acc[wave * G * D + h * D + lane * 8 + e] = acc[h][e];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
@@ -578,7 +684,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     for (int w = 0; w < W; ++w) {
       const float sc = fast_exp2(s_m[w][h] - M);
       L = fmaf(sc, s_l[w][h], L);
-      A = fmaf(sc, s_acc[w][e], A);
+      A = fmaf(sc, s_acc[w * G * D + e], A);
     }
     if (a.mode == PKV_MODE_UNSPLIT) {
       a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] =

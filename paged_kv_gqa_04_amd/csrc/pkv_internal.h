@@ -17,7 +17,10 @@ constexpr int kPageTokens = 16;
 // Waves (64 lanes each) in one partial-kernel workgroup. A workgroup owns
 // one (sequence, KV head, page range) item; its waves take the range's
 // pages round-robin and merge their states in LDS at the end.
-constexpr int kWavesPerGroup = 4;
+#ifndef PKV_WAVES_PER_GROUP
+#define PKV_WAVES_PER_GROUP 4
+#endif
+constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 
 // Work-queue item as the partial kernel reads it (16 bytes).
 struct Item {
