@@ -29,6 +29,9 @@ namespace pkv {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 #define GPTR(p) ((__attribute__((address_space(1))) void*)(p))
 #define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -136,11 +139,58 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+// Cross-row exchanges (gfx950): with both operands equal, permlane16_swap
+// returns each lane's value and that of the lane 16 away in the paired row;
+// permlane32_swap likewise across the two halves of the wave.
+__device__ __forceinline__ float swap16_add(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float swap32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over lane-index bits FROM..5 (the other bits fixed), result in every
+// lane: DPP quad permutes for bits 0-1, row rotations by 4 and 8 for bits
+// 2-3, row and half-wave swaps for bits 4-5. No LDS round trips.
+template <int FROM>
+__device__ __forceinline__ float sum_lanes_from(float v) {
+  if constexpr (FROM <= 0) v += dpp_mov<0xB1>(v);
+  if constexpr (FROM <= 1) v += dpp_mov<0x4E>(v);
+  if constexpr (FROM <= 2) v += dpp_mov<0x124>(v);
+  if constexpr (FROM <= 3) v += dpp_mov<0x128>(v);
+  if constexpr (FROM <= 4) v = swap16_add(v);
+  return swap32_add(v);
+}
+
+// Sum / max over the 16 lanes of each row (DPP only).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x124>(v);
+  return v + dpp_mov<0x128>(v);
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x124>(v));
+  return fmaxf(v, dpp_mov<0x128>(v));
+}
+
+// 16x16x32 matrix-core product on 8-element bf16 / fp16 operands held as
+// raw 16-byte vectors, fp32 accumulate.
+template <int DT>
+__device__ __forceinline__ floatx4 mfma_16x16x32(u32x4 a, u32x4 b, floatx4 c) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
 
 // Read one ring slot back from LDS: wait until at most VM vector-memory
 // loads are outstanding (the slot's own direct-to-LDS loads have landed),
@@ -174,7 +224,7 @@ __device__ __forceinline__ float wave_max(float v) {
 
 template <int LPP, int VM, typename KArr, typename VArr>
 __device__ __forceinline__ void read_slot(const uint32_t* ka, uint32_t va, KArr& k, VArr& v) {
-  u32x4* kk = &k[0][0];
+  u32x4* kk = &k[0];
   if constexpr (LPP == 8) {
     if constexpr (VM == 8) PKV_READ8("8");
     else if constexpr (VM == 16) PKV_READ8("16");
@@ -241,7 +291,7 @@ struct MergeParams {
 // m and l of neighbouring rows share cache lines and are read with
 // device-scope loads; a row's acc block is whole 128-byte lines that no
 // other workgroup reads, so plain loads see the device-scope stores.
-constexpr int kMergeBatch = 8;
+constexpr int kMergeBatch = 16;
 
 template <int DT, int G, int D>
 __device__ void merge_row(const float* ws_m, const float* ws_l, const float* ws_acc, int base,
@@ -340,53 +390,53 @@ __device__ void finish_group(const PartialParams& a, int b, int g) {
 
 // ---------------------------------------------------------- partial kernel
 //
-// Lane layouts inside a wave, for one 16-token page of one KV head (the
-// page tile is 16 x D contiguous elements):
-//  * K: LPT lanes per token (4, or 8 when D = 128 and G = 8); lane
-//    (t = lane / LPT, c = lane % LPT) holds elements
-//    {j*8*LPT + c*8 + i} of its token, so each 16-byte load instruction reads
-//    whole 64- or 128-byte runs of every token row. A page takes
-//    16*LPT/64 passes. q is held in the same layout, so q.k is D/LPT/2
-//    v_dot2 per head, then an LPT-lane DPP sum.
-//  * V: D/8 lanes per token; lane (r = lane / (D/8), c = lane % (D/8)) holds
-//    elements c*8 .. c*8+7, so one load instruction reads 64 consecutive
-//    16-byte pieces (1 KiB). acc[G][8] per lane; lanes with equal c and
-//    different r are summed once at the end of the range.
-//  * p (softmax weights) moves from the K layout to the V layout through a
-//    small per-wave LDS buffer.
-// Each wave keeps a wave-uniform reference maximum per head; it is raised
-// (with a rescale of l and acc) only when a logit exceeds it by kTau.
+// One workgroup (W waves) per (sequence b, KV head g, page range). Wave w
+// takes pages w, w+W, ... of the range. Per 16-token page of one KV head
+// (a 16 x D tile, contiguous in the pool):
+//  * K and V arrive in the wave's LDS ring by direct-to-LDS loads, each in
+//    1 KiB contiguous runs. K rows are stored with their 16-byte chunks
+//    rotated by the token index (chunk c of token t at slot position
+//    (c + t) mod (2D/16)): every lane still fetches whole row runs, and the
+//    MFMA operand reads below touch distinct LDS banks.
+//  * Logits: S^T = Q K^T on the matrix cores, v_mfma_f32_16x16x32 over d in
+//    D/32 steps. A = Q (16 rows: the G heads of the group, zero-padded),
+//    B = K^T (16 columns: the page's tokens). The 16x16 result gives lane l
+//    token l % 16 and heads 4 (l / 16) .. +3.
+//  * Softmax: one reference maximum per head, shared by the 16 lanes of a
+//    row, raised only when a logit exceeds it by kTau (then l and acc are
+//    rescaled). Masked tokens and padding heads get -inf by select.
+//  * P.V on the vector ALUs in fp32: lane (r = l / (D/8), c = l % (D/8))
+//    owns columns c*8 .. c*8+7 of the tokens r, r + 64/(D/8), ...; the V
+//    pieces it needs are exactly the ones its own DMA lane brought in.
+//    Softmax weights move from the MFMA layout to this one through a tiny
+//    per-wave LDS buffer. acc[G][8] per lane.
 template <int DT, int G, int D>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   constexpr int W = kWavesPerGroup;
   constexpr int P = kPageTokens;
-  constexpr int LPT = (D == 128 && G >= 8) ? 8 : 4;
-  constexpr int EK = D / LPT;    // K elements per lane per pass
-  constexpr int NKL = EK / 8;    // 16-byte K loads per lane per pass
-  constexpr int TPK = 64 / LPT;  // tokens per K pass
-  constexpr int NKP = P / TPK;   // K passes per page
-  constexpr int VL = D / 8;      // lanes per token in the V layout
-  constexpr int TPI = 64 / VL;   // tokens per V load instruction
-  constexpr int NVI = P / TPI;   // V loads per lane per page
-  constexpr int TILE = P * D;    // elements of one (page, KV head) tile
+  constexpr int NKI = D / 32;     // K: 1 KiB DMA runs per page = MFMA steps
+  constexpr int RB = D * 2;       // bytes per token row
+  constexpr int NCH = RB / 16;    // 16-byte chunks per token row
+  constexpr int VL = D / 8;       // lanes per token in the V layout
+  constexpr int TPI = 64 / VL;    // tokens per V load instruction
+  constexpr int NVI = P / TPI;    // V loads per lane per page
+  constexpr int TILE = P * D;     // elements of one (page, KV head) tile
+  constexpr int GR = (G + 3) / 4;  // 16-lane rows of the MFMA result holding real heads
+  static_assert(G <= 16, "one MFMA tile of heads");
 
-  constexpr int LPP = NKP * NKL + NVI;  // 16-byte load instructions per page
-  constexpr int NB = kRingSlots;        // ring slots per wave (pages)
+  constexpr int LPP = NKI + NVI;         // 16-byte load instructions per page
+  constexpr int NB = kRingSlots;         // ring slots per wave (pages)
   constexpr int SLOT_WORDS = LPP * 256;  // one slot: LPP x 64 lanes x 16 B
 
-  // K/V ring: each wave owns NB slots, filled by direct-to-LDS loads. Lane i
-  // of a load instruction lands at (instruction base + 16 i) and is read back
-  // by lane i itself, so the ring needs no registers and no bank-friendly
-  // layout. The ring is reused for the cross-wave combine at the end.
-  // One LDS array per slot (not one array indexed by slot): the compiler
-  // then sees that reading slot r cannot alias the loads still landing in
-  // the other slots and waits for slot r's loads only.
+  // K/V ring: each wave owns NB slots. One LDS array per slot (not one
+  // array indexed by slot) lets the compiler tell slots apart. The first
+  // array doubles as the cross-wave combine buffer at the end.
   static_assert(NB >= 2 && NB <= 4, "two to four slot arrays");
   __shared__ __attribute__((aligned(16))) uint32_t s_ring0[W * SLOT_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t s_ring1[W * SLOT_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t s_ring2[NB > 2 ? W * SLOT_WORDS : 4];
   __shared__ __attribute__((aligned(16))) uint32_t s_ring3[NB > 3 ? W * SLOT_WORDS : 4];
-  __shared__ float s_p[W][P * G];
+  __shared__ __attribute__((aligned(16))) float s_p[W][P * G];
   __shared__ float s_m[W][G];
   __shared__ float s_l[W][G];
   static_assert(G * D <= SLOT_WORDS, "combine buffer fits in one ring array");
@@ -444,51 +494,51 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     return;
   }
 
-  const int kt = lane / LPT, kc = lane % LPT;
-  const int vr = lane / VL, vc = lane % VL;
+  const int t16 = lane & 15;   // token of this lane in the MFMA result
+  const int hq = lane >> 4;    // head quad of this lane in the MFMA result
+  const int vr = lane / VL;
 
-  // K sits in its LDS slot exactly as in memory (token rows of D elements).
-  // Lane (kt, kc) takes, at step j, the 16*LPT-byte column block
-  // jr = (j + kt) % NKL of token kt: the rotation by token keeps the 16
-  // lanes of an LDS read phase on distinct banks. The dot product does not
-  // care about the order of d, so q is held in the same rotated order.
-  uint32_t qr[G][EK / 2];
-  uint32_t kofs[NKP * NKL];  // this lane's K byte offsets inside a slot
+  // Q as the MFMA A operand: row t16 = head of the group (zero past G),
+  // k = d in steps of 32: this lane holds d = 32 kk + 8 hq .. +7.
+  u32x4 qa[NKI];
   {
-    const uint16_t* qb = a.q + ((int64_t)b * a.num_q_heads + g * G) * D;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.num_q_heads + g * G + t16) * D;
 #pragma unroll
-    for (int j = 0; j < NKL; ++j) {
-      const int jr = (j + kt) % NKL;
+    for (int kk = 0; kk < NKI; ++kk)
+      qa[kk] = t16 < G ? *(const u32x4*)(qrow + 32 * kk + 8 * hq) : u32x4{0, 0, 0, 0};
+  }
+  // This lane's K operand bytes inside a slot (rotated chunks), and the
+  // global element offset its K DMA lanes fetch.
+  uint32_t kofs[NKI];
+  int kdma[NKI];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const u32x4 v = *(const u32x4*)(qb + h * D + jr * 8 * LPT + kc * 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) qr[h][j * 4 + w] = v[w];
-      }
-#pragma unroll
-      for (int pk = 0; pk < NKP; ++pk)
-        kofs[pk * NKL + j] = ((pk * TPK + kt) * D + jr * 8 * LPT + kc * 8) * 2;
-    }
+  for (int kk = 0; kk < NKI; ++kk) {
+    kofs[kk] = t16 * RB + ((4 * kk + hq + t16) % NCH) * 16;
+    const int pos = kk * 1024 + lane * 16;  // where DMA lane `lane` lands
+    const int t = pos / RB, pch = (pos % RB) / 16;
+    kdma[kk] = t * D + (((pch - t) % NCH + NCH) % NCH) * 8;  // t may exceed NCH
   }
 
   float acc[G][8];
-  float lsum[G], mref[G];
+  float lsum[4], mref[4];  // per head 4 hq + i, shared across a row
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lsum[h] = 0.0f;
-    mref[h] = kNoMax;
+  for (int i = 0; i < 4; ++i) {
+    lsum[i] = 0.0f;
+    mref[i] = kNoMax;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-  }
 
   // Block-table entries of the range are staged in LDS, kBtChunk at a time,
   // and read back with a broadcast LDS read: an in-loop vector load of the
-  // table would make the compiler drain every outstanding K/V prefetch.
+  // table would make the compiler drain every outstanding K/V load.
   __shared__ int32_t s_bt[kBtChunk];
   const int32_t* bt_row = a.block_table + (int64_t)b * a.stride;
 
   struct Page {
-    u32x4 k[NKP][NKL];
+    u32x4 kb[NKI];
     u32x4 v[NVI];
     int ntok;  // valid tokens of the page (0 if its table entry is bad)
   };
@@ -520,27 +570,26 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     const int on = real ? 1 : 0;  // lane offsets vanish for the filler loads
     uint32_t* dst = slot_base(sl);
 #pragma unroll
-    for (int i = 0; i < NKP * NKL; ++i)  // K: 1 KiB contiguous per instruction
-      __builtin_amdgcn_global_load_lds(GPTR(kp + on * (i * 512 + lane * 8)),
-                                       LPTR(dst + i * 256), 16, 0, kLoadNontemporal);
+    for (int kk = 0; kk < NKI; ++kk)
+      __builtin_amdgcn_global_load_lds(GPTR(kp + on * kdma[kk]), LPTR(dst + kk * 256), 16, 0,
+                                       kLoadNontemporal);
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
-      __builtin_amdgcn_global_load_lds(GPTR(vp + on * ((i * TPI + vr) * D + vc * 8)),
-                                       LPTR(dst + (NKP * NKL + i) * 256), 16, 0,
-                                       kLoadNontemporal);
+      __builtin_amdgcn_global_load_lds(GPTR(vp + on * (i * 512 + lane * 8)),
+                                       LPTR(dst + (NKI + i) * 256), 16, 0, kLoadNontemporal);
   };
 
   // Wait until slot `sl` has landed (the NB-1 younger pages may stay in
-  // flight), then read this lane's 16-byte pieces back. The wait and the LDS
+  // flight), then read this lane's operands back. The wait and the LDS
   // reads are one asm block: left to itself the compiler cannot tell the
   // ring slots apart at the loop back-edge and drains every load in flight.
   auto fetch_page = [&](int sl) -> Page {
     Page r;
     const uint32_t base = (uint32_t)(uintptr_t)LPTR(slot_base(sl));
-    uint32_t ka[NKP * NKL];
+    uint32_t ka[NKI];
 #pragma unroll
-    for (int i = 0; i < NKP * NKL; ++i) ka[i] = base + kofs[i];
-    read_slot<LPP, (NB - 1) * LPP>(ka, base + (NKP * NKL) * 1024 + lane * 16, r.k, r.v);
+    for (int i = 0; i < NKI; ++i) ka[i] = base + kofs[i];
+    read_slot<LPP, (NB - 1) * LPP>(ka, base + NKI * 1024 + lane * 16, r.kb, r.v);
     r.ntok = ntok_ring[sl];
     return r;
   };
@@ -548,54 +597,49 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   float* sp = s_p[wave];
 
   auto compute_page = [&](const Page& r) {
+    floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < NKI; ++kk) c = mfma_16x16x32<DT>(qa[kk], r.kb[kk], c);
     // logits, log2 domain, masked by select (never by multiply: tails may
-    // hold NaN).
-    float x[NKP][G];
-#pragma unroll
-    for (int pk = 0; pk < NKP; ++pk) {
-      const bool valid = (pk * TPK + kt) < r.ntok;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NKL; ++j)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) s = dot2<DT>(r.k[pk][j][w], qr[h][j * 4 + w], s);
-        s = group_sum<LPT>(s);
-        x[pk][h] = valid ? s * a.scale_log2 : -INFINITY;
-      }
-    }
+    // hold NaN)
+    const bool tok_ok = t16 < r.ntok;
+    float x[4];
     bool need = false;
 #pragma unroll
-    for (int pk = 0; pk < NKP; ++pk)
-#pragma unroll
-      for (int h = 0; h < G; ++h) need |= x[pk][h] > mref[h] + kTau;
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = tok_ok && (4 * hq + i < G);
+      x[i] = ok ? c[i] * a.scale_log2 : -INFINITY;
+      need |= x[i] > mref[i] + kTau;
+    }
     if (__any(need)) {
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mn = fmaxf(mref[i], row16_max(x[i]));
+        alpha[i] = fast_exp2(mref[i] - mn);
+        lsum[i] *= alpha[i];
+        mref[i] = mn;
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float pm = x[0][h];
+        const float al = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(alpha[h % 4]), 16 * (h / 4)));
 #pragma unroll
-        for (int pk = 1; pk < NKP; ++pk) pm = fmaxf(pm, x[pk][h]);
-        pm = wave_max(pm);
-        const float mnew = fmaxf(mref[h], pm);
-        const float alpha = fast_exp2(mref[h] - mnew);
-        lsum[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-        mref[h] = mnew;
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
       }
     }
+    float p[4];
 #pragma unroll
-    for (int pk = 0; pk < NKP; ++pk) {
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(x[i] - mref[i]);
+      lsum[i] += p[i];
+    }
+    if (hq < GR) {
+      if constexpr (G >= 4) {
+        *(float4*)(sp + t16 * G + 4 * hq) = make_float4(p[0], p[1], p[2], p[3]);
+      } else {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = fast_exp2(x[pk][h] - mref[h]);
-        x[pk][h] = p;
-        lsum[h] += p;
-      }
-      if (kc == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) sp[(pk * TPK + kt) * G + h] = x[pk][h];
+        for (int i = 0; i < G; ++i) sp[t16 * G + i] = p[i];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -634,6 +678,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     __syncthreads();
     cnt = span > wave ? (span - wave + W - 1) / W : 0;
     if (cnt == 0) continue;
+    // Nothing else is in flight here (q and the table have landed); saying
+    // so keeps the compiler from guarding the q registers inside the ring.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) issue_page(i, i);
     for (int k = 0; k < cnt; k += NB) {
@@ -649,23 +696,27 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   }
 
   // ---- combine the wave states, then the workgroup's waves ----
+  // l: sum over the 16 tokens of each MFMA row; acc: over the V rows.
+  constexpr int LOG2_VL = VL == 16 ? 4 : 3;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int i = 0; i < 4; ++i) lsum[i] = row16_sum(lsum[i]);
 #pragma unroll
-    for (int m = LPT; m < 64; m <<= 1) lsum[h] += __shfl_xor(lsum[h], m);
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int m = VL; m < 64; m <<= 1) acc[h][e] += __shfl_xor(acc[h][e], m);
-  }
+    for (int e = 0; e < 8; ++e) acc[h][e] = sum_lanes_from<LOG2_VL>(acc[h][e]);
   float* s_acc = reinterpret_cast<float*>(s_ring0);  // [W][G * D], ring is done
   __syncthreads();
-  if (lane == 0) {
+  // Each row's first lane writes its own heads. (A readlane from another
+  // lane inside a lane-0-only branch is not safe: the compiler may sink the
+  // last step of the row sum into the branch, leaving the other lane's
+  // value unfinished.)
+  if (t16 == 0 && hq < GR) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_m[wave][h] = mref[h];
-      s_l[wave][h] = lsum[h];
-    }
+    for (int i = 0; i < 4; ++i)
+      if (4 * hq + i < G) {
+        s_m[wave][4 * hq + i] = mref[i];
+        s_l[wave][4 * hq + i] = lsum[i];
+      }
   }
   if (lane < VL) {
 #pragma unroll
