@@ -158,6 +158,30 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
     }
 
 
+def sweep(P, dev, spec, replicas, ev, a):
+    """Policy calibration: time unsplit, split over a range of S and the work
+    queue over a range of chunk sizes, plus the policy's own choice."""
+    lens = np.asarray(dev["seq_lens_host"])
+    max_pages = int((lens.max() + 15) // 16)
+    cands = [("auto", 0, 0), ("unsplit", 0, 0)]
+    for S in (2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 192, 256):
+        if S <= max_pages:
+            cands.append(("split", S, 0))
+    for c in (4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512, 1024, 2048):
+        if c <= max_pages:
+            cands.append(("workqueue", 0, c))
+    for mode, S, c in cands:
+        r = time_mode(P, dev, spec, mode, S, c, a.steps, a.warmup, replicas, ev, a.merge)
+        st = r["stats"]
+        print(json.dumps({
+            "workload": spec.name, "seed": a.seed, "mode": mode,
+            "resolved": st["mode_name"], "num_splits": st["num_splits"],
+            "chunk_pages": st["chunk_pages"], "grid": st["grid"],
+            "us_per_step": round(r["step_us"], 2),
+            "gbps": round(st["algorithmic_bytes"] / (r["step_us"] * 1e-6) / 1e9, 1),
+        }), flush=True)
+
+
 def cpu_baseline(case, target_s=10.0, cap_s=30.0):
     """Time the CPU oracle on the bench workload until ~target_s of work."""
     from oracle import paged_gqa as O
@@ -192,6 +216,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-auto", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time a grid of (mode, splits / chunk) candidates for the "
+                         "workload, one JSON line each (policy calibration)")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -221,6 +248,9 @@ def main():
     dev["replicas"] = reps
     ev = HipEvents()
 
+    if a.sweep:
+        sweep(P, dev, spec, replicas, ev, a)
+        return
     r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev, a.merge)
     st = r["stats"]
     B = len(dev["seq_lens_host"])

@@ -42,23 +42,26 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // --- Policy constants (MI355X) -------------------------------------------
-// Items the partial kernel should expose per compute unit before splitting
-// stops paying: enough resident workgroups that every CU keeps several
-// pages of K/V in flight.
-constexpr int kTargetItemsPerCU = 2;
-// Smallest range worth a workgroup (pages): one page per wave at least two
-// times over, so each wave pipelines loads behind compute.
+// Measured on an MI355X (256 CUs) with the calibration seed (20260622) over
+// the long, mixed B=8, B=4 and B=64 workloads: one work item per CU is best
+// while items stay short (a single split-S row: S = 32 beat 64 by 10%; B=4
+// and B=8 ragged batches likewise); very large batches want items of at most
+// ~512 pages so the longest-first queue stays balanced (within 2% from 256
+// to 1024; a whole-row unsplit launch of the B=64 batch was 2x slower).
+constexpr int kTargetItemsPerCU = 1;
+constexpr int kMaxChunkPages = 512;
+// Smallest range worth a workgroup (pages): two pages per wave.
 constexpr int kMinChunkPages = 2 * kWavesPerGroup;
 
 int32_t pages_of(int32_t n) { return (int32_t)ceil_div(n, kPageTokens); }
 
-// Chunk (pages per range) that brings the item count near the target.
+// Pages per range that spread the step's page-heads over one item per CU.
 int32_t auto_chunk(const pkv_plan& p, int64_t total_pages) {
   int64_t target = (int64_t)p.num_cus * kTargetItemsPerCU;
   int64_t work = total_pages * p.shape.num_kv_heads;
-  int64_t c = std::max<int64_t>(kMinChunkPages, ceil_div(work, std::max<int64_t>(1, target)));
-  c = align_up(c, kWavesPerGroup);
-  return (int32_t)std::min<int64_t>(c, INT32_MAX / 2);
+  int64_t c = ceil_div(work, std::max<int64_t>(1, target));
+  c = std::min<int64_t>(std::max<int64_t>(c, kMinChunkPages), kMaxChunkPages);
+  return (int32_t)align_up(c, kWavesPerGroup);
 }
 
 uint64_t splitmix64(uint64_t& s) {
@@ -159,16 +162,14 @@ pkv_status build(pkv_plan& p) {
     return PKV_ERR_INVALID;
   }
   p.fused = p.opts.merge == PKV_MERGE_FUSED;
-  const int64_t target = (int64_t)p.num_cus * kTargetItemsPerCU;
   int32_t chunk = p.opts.chunk_pages > 0 ? p.opts.chunk_pages : auto_chunk(p, total_pages);
   if (mode == PKV_MODE_AUTO) {
-    const int64_t units = (int64_t)active * Hkv;
-    if (units == 0 || units >= target || max_pages <= chunk) {
-      mode = PKV_MODE_UNSPLIT;  // enough rows, or nothing worth splitting
+    if (active == 0 || max_pages <= chunk) {
+      mode = PKV_MODE_UNSPLIT;  // every row fits in one item: nothing to merge
     } else if (same_len) {
       mode = PKV_MODE_SPLIT;  // equal rows: the rectangular grid wastes nothing
     } else {
-      mode = PKV_MODE_WORKQUEUE;
+      mode = PKV_MODE_WORKQUEUE;  // ragged rows: only non-empty ranges
     }
   }
 
