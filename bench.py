@@ -98,6 +98,29 @@ def partial_kernel_bytes(stats, spec, batch):
     return b + (out_bytes if stats["mode_name"] == "unsplit" else 0)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "partial_kernel_long_split32_traffic.md")
+
+
+def measured_traffic(workload, mode, splits, merge):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, scaled by the plain-copy factors it
+    records; None when the workload differs from the profiled one or the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    if (workload, mode, splits, merge) != ("long", "split", 32, "fused"):
+        return None
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = open(os.path.join(ROOT, "paged_kv_gqa_04_amd", "csrc", "decode.hip"), "rb").read()
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines()
+                  if l.startswith(("traffic_bytes_per_launch:", "kernel_source_sha256:")))
+    if fields.get("kernel_source_sha256", "").strip() != hashlib.sha256(src).hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, merge="fused"):
     """Time `steps` back-to-back decode steps (one event pair around all of
     them: per-step markers would add their own overhead), then the same
@@ -216,6 +239,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-auto", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes 5 times "
+                         "(reference kernel for scaling rocprof byte counters)")
     ap.add_argument("--sweep", action="store_true",
                     help="time a grid of (mode, splits / chunk) candidates for the "
                          "workload, one JSON line each (policy calibration)")
@@ -227,6 +253,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if a.copy_bytes:
+        src = torch.ones(a.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.copy_bytes, "calls": 5}))
+        return
 
     import paged_kv_gqa_04_amd as P
     import workloads as W
@@ -298,7 +333,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(part_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(spec.name, st["mode_name"], st["num_splits"], a.merge),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)",
             "bytes_per_launch": int(part_bytes),
             "avg_launch_us": round(kern_us, 2),
         },
