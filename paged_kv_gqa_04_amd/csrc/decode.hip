@@ -53,6 +53,7 @@ constexpr int kThreads = kWavesPerGroup * 64;
 constexpr int kRingSlots = PKV_RING_SLOTS;
 // Block-table entries staged in LDS at a time by the partial kernel.
 constexpr int kBtChunk = 512;
+static_assert(kBtChunk % kThreads == 0, "table staging: whole rounds of the workgroup");
 // s_waitcnt immediate for gfx9: vmcnt(n) (6 bits: [3:0] and [15:14]) with
 // expcnt(7) and lgkmcnt(15), i.e. wait on vector-memory loads only.
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
@@ -109,18 +110,19 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One step of the exact merge of partial states: (M, L, A) <- (M, L, A)
-// combined with (m, l, a); a state with m = -inf is neutral.
-__device__ __forceinline__ void merge4(float& M, float& L, float4& A, float m, float l, float4 a) {
-  const float mn = fmaxf(M, m);
-  const float co = M == -INFINITY ? 0.0f : fast_exp2(M - mn);
-  const float cn = m == -INFINITY ? 0.0f : fast_exp2(m - mn);
-  L = L * co + l * cn;
-  A.x = A.x * co + a.x * cn;
-  A.y = A.y * co + a.y * cn;
-  A.z = A.z * co + a.z * cn;
-  A.w = A.w * co + a.w * cn;
-  M = mn;
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 V#: stride 0, 32-bit
+// data format); a load past the end returns zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kCpolSc1 = 16;  // cache-policy operand: device (agent) scope
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes,
+                                           kRawBufferWord3);
+}
+// 16 bytes of a partial state at byte offset `off`, device-scope load.
+__device__ __forceinline__ float4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc1);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
 }
 
 template <int CTRL>
@@ -151,6 +153,15 @@ __device__ __forceinline__ float swap32_add(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ float swap16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sum over lane-index bits FROM..5 (the other bits fixed), result in every
 // lane: DPP quad permutes for bits 0-1, row rotations by 4 and 8 for bits
 // 2-3, row and half-wave swaps for bits 4-5. No LDS round trips.
@@ -162,6 +173,17 @@ __device__ __forceinline__ float sum_lanes_from(float v) {
   if constexpr (FROM <= 3) v += dpp_mov<0x128>(v);
   if constexpr (FROM <= 4) v = swap16_add(v);
   return swap32_add(v);
+}
+
+// Maximum over lane-index bits FROM..5, same exchanges as sum_lanes_from.
+template <int FROM>
+__device__ __forceinline__ float max_lanes_from(float v) {
+  if constexpr (FROM <= 0) v = fmaxf(v, dpp_mov<0xB1>(v));
+  if constexpr (FROM <= 1) v = fmaxf(v, dpp_mov<0x4E>(v));
+  if constexpr (FROM <= 2) v = fmaxf(v, dpp_mov<0x124>(v));
+  if constexpr (FROM <= 3) v = fmaxf(v, dpp_mov<0x128>(v));
+  if constexpr (FROM <= 4) v = swap16_max(v);
+  return swap32_max(v);
 }
 
 // Sum / max over the 16 lanes of each row (DPP only).
@@ -260,6 +282,7 @@ struct PartialParams {
   int32_t num_q_heads;
   int32_t mode;
   int32_t num_splits;
+  int32_t split_chunk;  // SPLIT: range size shared by every row (0: per row, from seq_lens)
   int32_t fused;     // last-arriving workgroup of a row merges its states
   float scale_log2;  // sm_scale * log2(e)
 };
@@ -280,69 +303,146 @@ struct MergeParams {
 // ------------------------------------------------------------ state merge
 //
 // Merge the `count` partial states of one (sequence, KV head) row, slots
-// base .. base+count-1, into the row's G x D outputs. Run by a whole
-// workgroup: thread t owns a 4-float column c of the G x D state and the
-// slots s = t / NC, t / NC + NSUB, ... (NSUB column groups side by side), so
-// one round of loads covers up to NSUB * kMergeBatch slots; the subsets are
-// then combined in subset order. The order of operations depends only on
-// the slot indices, never on timing, so the fused tail and the separate
-// merge kernel (both call this) produce the same bits.
-//
-// m and l of neighbouring rows share cache lines and are read with
-// device-scope loads; a row's acc block is whole 128-byte lines that no
-// other workgroup reads, so plain loads see the device-scope stores.
-constexpr int kMergeBatch = 16;
+// base .. base+count-1, into the row's G x D outputs, in the two passes of
+// the definition (PersistentKV explainer, Methodology 1: the merge kernel
+// combines the split states exactly): per head M = max_s m_s, weights
+// w_s = 2^(m_s - M) (0 for a neutral state), L = sum_s w_s l_s, then
+// out = sum_s w_s acc_s / L (0 when L = 0: an empty row). Run by a whole
+// workgroup:
+//  * acc: thread t owns float4 column t % NC of the G x D state and the
+//    slots t / NC, t / NC + NSUB, ...; its first batch of loads is issued
+//    first, so that it shares one memory latency with the m / l loads.
+//  * m / l: every wave reads all of them itself (lane = slot * G + head,
+//    K lane rounds), reduces each head with fixed DPP / permlane trees and
+//    writes its weights to its own LDS area: no cross-wave barrier.
+//  * the NSUB column-owner subsets are added in subset order at the end.
+// Every reduction order is fixed by the slot indices alone, never by
+// timing, so the fused tail and the separate merge kernel (both call this)
+// produce the same bits. All state loads are device-scope: the states come
+// from workgroups on other XCDs.
+constexpr int kMergeBatch = 16;  // acc loads in flight per thread
 
 template <int DT, int G, int D>
-__device__ void merge_row(const float* ws_m, const float* ws_l, const float* ws_acc, int base,
-                          int count, uint16_t* out_row) {
-  constexpr int NC = G * D / 4;       // float4 columns of one state
-  constexpr int NSUB = kThreads / NC;  // slot subsets merged side by side
+__device__ __forceinline__ void merge_row(const float* __restrict__ ws_m,
+                                          const float* __restrict__ ws_l,
+                                          const float* __restrict__ ws_acc, int base, int count,
+                                          uint16_t* __restrict__ out_row) {
+  constexpr int NC = G * D / 4;          // float4 columns of one state
+  constexpr int NSUB = kThreads / NC;    // slot subsets accumulated side by side
+  constexpr int PER = kMergeBatch;
+  constexpr int SB = PER * NSUB;         // slots per acc batch
+  constexpr int SPW = 64 / G;            // slots per lane round
+  constexpr int K = 4;                   // lane rounds per weight round
+  constexpr int TPH = K * SPW;           // slots per weight round
+  constexpr int W = kWavesPerGroup;
+  constexpr int LOG2G = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
   static_assert(NSUB >= 1 && NSUB * NC == kThreads, "layout");
-  __shared__ float s_M[NSUB][G], s_L[NSUB][G];
-  __shared__ float4 s_A[NSUB][NC];
-  const int t = threadIdx.x;
+  static_assert(SB <= TPH && TPH % SB == 0 && (1 << LOG2G) == G, "batches tile a round");
+  __shared__ float s_w[W][K * 64];  // per wave: weights of one round, [slot][head]
+  __shared__ float4 s_A[NSUB > 1 ? NSUB : 1][NC];
+  base = __builtin_amdgcn_readfirstlane(base);  // uniform: one buffer resource
+  count = __builtin_amdgcn_readfirstlane(count);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t % NC, sub = t / NC;
-  const int h = (c * 4) / D;
-  float M = -INFINITY, L = 0.0f;
-  float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  int s = sub;
-  for (; s + (kMergeBatch - 1) * NSUB < count; s += kMergeBatch * NSUB) {
-    float mv[kMergeBatch], lv[kMergeBatch];
-    float4 av[kMergeBatch];
+  const int hc = (c * 4) / D;  // head of this thread's acc column
+  const int hm = lane % G;     // head of this lane's m / l
+  const int sl = lane / G;     // slot (within a lane round) of this lane's m / l
+
+  // The row's acc states as one buffer: slots past `count` read as zeros.
+  const __amdgpu_buffer_rsrc_t racc =
+      raw_rsrc(ws_acc + (int64_t)base * (G * D), (uint32_t)count * (G * D * 4));
+  float4 av[PER];
+  auto load_acc = [&](int s0) {
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int64_t st = base + s + j * NSUB;
-      mv[j] = ld_agent(ws_m + st * G + h);
-      lv[j] = ld_agent(ws_l + st * G + h);
-      av[j] = *(const float4*)(ws_acc + st * (G * D) + c * 4);
+    for (int j = 0; j < PER; ++j)
+      av[j] = ld_agent16(racc, (uint32_t)((s0 + sub + j * NSUB) * (G * D) + c * 4) * 4u);
+  };
+  load_acc(0);
+
+  float mk[K];
+  auto load_m = [&](int r0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int s = r0 + k * SPW + sl;
+      mk[k] = s < count ? ld_agent(ws_m + (int64_t)(base + s) * G + hm) : -INFINITY;
+    }
+  };
+
+  // Pass 1: running (max, rescaled sum) per lane, then per head.
+  float Mt = -INFINITY, Lt = 0.0f;
+  for (int r0 = 0; r0 < count; r0 += TPH) {
+    float lk[K];
+    load_m(r0);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int s = r0 + k * SPW + sl;
+      lk[k] = s < count ? ld_agent(ws_l + (int64_t)(base + s) * G + hm) : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) merge4(M, L, A, mv[j], lv[j], av[j]);
+    for (int k = 0; k < K; ++k) {
+      const float mn = fmaxf(Mt, mk[k]);
+      Lt = (Mt == -INFINITY ? 0.0f : Lt * fast_exp2(Mt - mn)) +
+           (mk[k] == -INFINITY ? 0.0f : lk[k] * fast_exp2(mk[k] - mn));
+      Mt = mn;
+    }
   }
-  for (; s < count; s += NSUB) {
-    const int64_t st = base + s;
-    merge4(M, L, A, ld_agent(ws_m + st * G + h), ld_agent(ws_l + st * G + h),
-           *(const float4*)(ws_acc + st * (G * D) + c * 4));
+  const float M = max_lanes_from<LOG2G>(Mt);
+  const float L = sum_lanes_from<LOG2G>(Mt == -INFINITY ? 0.0f : Lt * fast_exp2(Mt - M));
+  const float Lc = __shfl(L, hc);  // lane hc holds head hc
+
+  // Pass 2: weights once per (slot, head), then the weighted acc sums.
+  float* sw = s_w[wave];
+  float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int r0 = 0; r0 < count; r0 += TPH) {
+    if (count > TPH) load_m(r0);  // else pass 1 left this round's m in mk
+#pragma unroll
+    for (int k = 0; k < K; ++k) sw[k * 64 + lane] = mk[k] == -INFINITY ? 0.0f : fast_exp2(mk[k] - M);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int r1 = min(count, r0 + TPH);
+    for (int b0 = r0; b0 < r1; b0 += SB) {
+      if (b0 > 0) load_acc(b0);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const float w = sw[(b0 - r0 + sub + j * NSUB) * G + hc];
+        A.x = fmaf(w, av[j].x, A.x);
+        A.y = fmaf(w, av[j].y, A.y);
+        A.z = fmaf(w, av[j].z, A.z);
+        A.w = fmaf(w, av[j].w, A.w);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // this round's weights are read
   }
   if constexpr (NSUB > 1) {
     s_A[sub][c] = A;
-    if ((c * 4) % D == 0) {
-      s_M[sub][h] = M;
-      s_L[sub][h] = L;
-    }
     __syncthreads();
     if (sub == 0) {
 #pragma unroll
-      for (int u = 1; u < NSUB; ++u) merge4(M, L, A, s_M[u][h], s_L[u][h], s_A[u][c]);
+      for (int u = 1; u < NSUB; ++u) {
+        const float4 o = s_A[u][c];
+        A.x += o.x;
+        A.y += o.y;
+        A.z += o.z;
+        A.w += o.w;
+      }
     }
   }
   if (sub == 0) {
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float inv = Lc > 0.0f ? 1.0f / Lc : 0.0f;
     const uint32_t lo = pack1<DT>(A.x * inv) | ((uint32_t)pack1<DT>(A.y * inv) << 16);
     const uint32_t hi = pack1<DT>(A.z * inv) | ((uint32_t)pack1<DT>(A.w * inv) << 16);
     *(uint2*)(out_row + c * 4) = make_uint2(lo, hi);
   }
+}
+
+// Slots of (sequence b, KV head g): (first slot, count). Split grid: S cells
+// per row in cell order. Work queue: sequence b's table entry (first slot of
+// the sequence, S_b), KV head g's S_b slots following one another.
+__device__ __forceinline__ SeqMeta row_slots(const PartialParams& a, int b, int g, SeqMeta wq) {
+  if (a.mode == PKV_MODE_WORKQUEUE) return {wq.slot_base + g * wq.splits, wq.splits};
+  return {(b * a.num_kv_heads + g) * a.num_splits, a.num_splits};
 }
 
 // --------------------------------------------------- fused merge (tail)
@@ -361,18 +461,10 @@ __device__ void merge_row(const float* ws_m, const float* ws_l, const float* ws_
 // full agent-scope fence would instead write back and invalidate the whole
 // L2 of the XCD, stalling every other workgroup there.
 template <int DT, int G, int D>
-__device__ void finish_group(const PartialParams& a, int b, int g) {
+__device__ void finish_group(const PartialParams& a, int b, int g, SeqMeta row) {
   __shared__ int s_last;
   const int bg = b * a.num_kv_heads + g;
-  int base, count;
-  if (a.mode == PKV_MODE_WORKQUEUE) {
-    const SeqMeta sm = a.meta[b];
-    count = sm.splits;
-    base = sm.slot_base + g * count;
-  } else {
-    count = a.num_splits;
-    base = bg * count;
-  }
+  const int base = row.slot_base, count = row.splits;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's state stores are done
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -447,6 +539,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
 
   // ---- which range this workgroup owns ----
   int b, g, pb, pe, slot = 0;
+  bool early = false;  // range known before the row length
   if (a.mode == PKV_MODE_WORKQUEUE) {
     const Item it = a.items[blockIdx.x];
     b = it.bg / Hkv;
@@ -454,6 +547,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     pb = it.page_begin;
     pe = it.page_end;
     slot = it.slot;
+    early = true;
   } else if (a.mode == PKV_MODE_SPLIT) {
     const int S = a.num_splits;
     const int cell = blockIdx.x;
@@ -461,10 +555,16 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     const int bg = cell / S;
     b = bg / Hkv;
     g = bg - b * Hkv;
-    const int pages = (a.seq_lens[b] + P - 1) / P;
-    const int chunk = pages > 0 ? (pages + S - 1) / S : 1;  // row-local
-    pb = s * chunk;
-    pe = min(pb + chunk, pages);
+    if (a.split_chunk > 0) {  // every row has this range size
+      pb = s * a.split_chunk;
+      pe = pb + a.split_chunk;
+      early = true;
+    } else {
+      const int pages = (a.seq_lens[b] + P - 1) / P;
+      const int chunk = pages > 0 ? (pages + S - 1) / S : 1;  // row-local
+      pb = s * chunk;
+      pe = min(pb + chunk, pages);
+    }
     slot = cell;
   } else {
     b = blockIdx.x / Hkv;
@@ -472,7 +572,57 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     pb = 0;
     pe = 0x7fffffff;
   }
+  // The row's partial-state slots, for the merge in the tail (the work
+  // queue's per-row table is loaded here, off the tail's critical path).
+  // It is a vector load (an atomic one: the compiler would otherwise pick a
+  // scalar load, and the next wait on any scalar load would wait for it),
+  // left undefined in the other modes so no register copy waits for it here.
+  SeqMeta qrow_meta;
+  if (a.mode == PKV_MODE_WORKQUEUE) {
+    const uint64_t v = __hip_atomic_load(
+        reinterpret_cast<uint64_t*>(const_cast<SeqMeta*>(a.meta + b)), __ATOMIC_RELAXED,
+        __HIP_MEMORY_SCOPE_WORKGROUP);
+    qrow_meta = {(int32_t)(uint32_t)v, (int32_t)(uint32_t)(v >> 32)};
+  }
+
+  const int t16 = lane & 15;   // token of this lane in the MFMA result
+  const int hq = lane >> 4;    // head quad of this lane in the MFMA result
+  const int vr = lane / VL;
+
+  // Q as the MFMA A operand: row t16 = head t16 of the group, k = d in steps
+  // of 32: this lane holds d = 32 kk + 8 hq .. +7. Rows past G repeat real
+  // heads (their logits are masked out), so every lane loads unconditionally
+  // and the loads overlap the table and length loads below.
+  u32x4 qa[NKI];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * a.num_q_heads + g * G + (t16 % G)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKI; ++kk) qa[kk] = *(const u32x4*)(qrow + 32 * kk + 8 * hq);
+  }
+
+  // Block-table entries of the range are staged in LDS, kBtChunk at a time,
+  // and read back with a broadcast LDS read: an in-loop vector load of the
+  // table would make the compiler drain every outstanding K/V load. When the
+  // range is known without the row length, the first chunk is fetched right
+  // away (entries inside the table row only), overlapping the length load.
+  __shared__ int32_t s_bt[kBtChunk];
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.stride;
+  auto stage_table = [&](int c0, int span) {  // all loads first, then the LDS writes
+    constexpr int U = kBtChunk / kThreads;
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      v[u] = i < span ? bt_row[c0 + i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      if (i < span) s_bt[i] = v[u];
+    }
+  };
   const int n = a.seq_lens[b];
+  if (early) stage_table(pb, min(min(pe, a.stride) - pb, kBtChunk));
   // Never past the device's own length, nor past the block-table row.
   pe = min(pe, min((n + P - 1) / P, a.stride));
 
@@ -490,23 +640,11 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
         }
       }
     }
-    if (a.mode != PKV_MODE_UNSPLIT && a.fused && slot >= 0) finish_group<DT, G, D>(a, b, g);
+    if (a.mode != PKV_MODE_UNSPLIT && a.fused && slot >= 0)
+      finish_group<DT, G, D>(a, b, g, row_slots(a, b, g, qrow_meta));
     return;
   }
 
-  const int t16 = lane & 15;   // token of this lane in the MFMA result
-  const int hq = lane >> 4;    // head quad of this lane in the MFMA result
-  const int vr = lane / VL;
-
-  // Q as the MFMA A operand: row t16 = head of the group (zero past G),
-  // k = d in steps of 32: this lane holds d = 32 kk + 8 hq .. +7.
-  u32x4 qa[NKI];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.num_q_heads + g * G + t16) * D;
-#pragma unroll
-    for (int kk = 0; kk < NKI; ++kk)
-      qa[kk] = t16 < G ? *(const u32x4*)(qrow + 32 * kk + 8 * hq) : u32x4{0, 0, 0, 0};
-  }
   // This lane's K operand bytes inside a slot (rotated chunks), and the
   // global element offset its K DMA lanes fetch.
   uint32_t kofs[NKI];
@@ -530,12 +668,6 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-
-  // Block-table entries of the range are staged in LDS, kBtChunk at a time,
-  // and read back with a broadcast LDS read: an in-loop vector load of the
-  // table would make the compiler drain every outstanding K/V load.
-  __shared__ int32_t s_bt[kBtChunk];
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.stride;
 
   struct Page {
     u32x4 kb[NKI];
@@ -674,7 +806,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   for (; cb < pe; cb += kBtChunk) {
     const int span = min(pe - cb, kBtChunk);
     if (cb != pb) __syncthreads();  // every wave is done with the last chunk
-    for (int i = threadIdx.x; i < span; i += kThreads) s_bt[i] = bt_row[cb + i];
+    if (cb != pb || !early) stage_table(cb, span);
     __syncthreads();
     cnt = span > wave ? (span - wave + W - 1) / W : 0;
     if (cnt == 0) continue;
@@ -748,7 +880,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
       }
     }
   }
-  if (a.mode != PKV_MODE_UNSPLIT && a.fused) finish_group<DT, G, D>(a, b, g);
+  if (a.mode != PKV_MODE_UNSPLIT && a.fused)
+    finish_group<DT, G, D>(a, b, g, row_slots(a, b, g, qrow_meta));
 }
 
 // ------------------------------------------------------------ merge kernel
@@ -887,6 +1020,7 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
   pp.num_q_heads = s.num_q_heads;
   pp.mode = p->mode;
   pp.num_splits = p->num_splits;
+  pp.split_chunk = p->split_chunk;
   pp.scale_log2 = s.sm_scale * kLog2e;
 
   hipError_t e;

@@ -48,6 +48,7 @@ struct pkv_plan {
   int32_t mode = PKV_MODE_UNSPLIT;
   int32_t num_splits = 1;  // S
   int32_t chunk_pages = 0;
+  int32_t split_chunk = 0;  // SPLIT with one page count for every row: its range size
   int32_t grid = 0;
   int32_t num_items = 0;
   int32_t empty_items = 0;

@@ -43,11 +43,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // --- Policy constants (MI355X) -------------------------------------------
 // Measured on an MI355X (256 CUs) with the calibration seed (20260622) over
-// the long, mixed B=8, B=4 and B=64 workloads: one work item per CU is best
-// while items stay short (a single split-S row: S = 32 beat 64 by 10%; B=4
-// and B=8 ragged batches likewise); very large batches want items of at most
-// ~512 pages so the longest-first queue stays balanced (within 2% from 256
-// to 1024; a whole-row unsplit launch of the B=64 batch was 2x slower).
+// the long, mixed B=8, B=4 and B=64 workloads: the step is fastest when every
+// CU runs at most one work item (a single split-S row: S = 32 beat 64 by 10%;
+// on ragged B=4 and B=8 batches the best range size was the smallest one
+// whose item count, after rounding each row up, fits the CUs: items of a
+// second workgroup on some CUs finish late). Batches too large for that
+// want items of at most ~512 pages so the longest-first queue stays
+// balanced (within 2% from 256 to 1024; a whole-row unsplit launch of the
+// B=64 batch was 2x slower).
 constexpr int kTargetItemsPerCU = 1;
 constexpr int kMaxChunkPages = 512;
 // Smallest range worth a workgroup (pages): two pages per wave.
@@ -55,13 +58,24 @@ constexpr int kMinChunkPages = 2 * kWavesPerGroup;
 
 int32_t pages_of(int32_t n) { return (int32_t)ceil_div(n, kPageTokens); }
 
-// Pages per range that spread the step's page-heads over one item per CU.
+// Work items (ranges of at most c pages, per row and KV head) of the step.
+int64_t items_at(const pkv_plan& p, int64_t c) {
+  int64_t n = 0;
+  for (int32_t len : p.seq_lens) n += ceil_div(pages_of(len), c);
+  return n * p.shape.num_kv_heads;
+}
+
+// Range size: the smallest multiple of the wave count, from the even share
+// of the step's page-heads per CU up to kMaxChunkPages, whose items (each
+// row rounded up separately) fit one per CU.
 int32_t auto_chunk(const pkv_plan& p, int64_t total_pages) {
-  int64_t target = (int64_t)p.num_cus * kTargetItemsPerCU;
-  int64_t work = total_pages * p.shape.num_kv_heads;
-  int64_t c = ceil_div(work, std::max<int64_t>(1, target));
-  c = std::min<int64_t>(std::max<int64_t>(c, kMinChunkPages), kMaxChunkPages);
-  return (int32_t)align_up(c, kWavesPerGroup);
+  const int64_t target = std::max<int64_t>(1, (int64_t)p.num_cus * kTargetItemsPerCU);
+  const int64_t work = total_pages * p.shape.num_kv_heads;
+  int64_t c = std::min<int64_t>(std::max<int64_t>(ceil_div(work, target), kMinChunkPages),
+                                kMaxChunkPages);
+  c = align_up(c, kWavesPerGroup);
+  while (c < kMaxChunkPages && items_at(p, c) > target) c += kWavesPerGroup;
+  return (int32_t)c;
 }
 
 uint64_t splitmix64(uint64_t& s) {
@@ -176,6 +190,7 @@ pkv_status build(pkv_plan& p) {
   p.items.clear();
   p.meta.clear();
   p.mode = mode;
+  p.split_chunk = 0;
   p.kv_tokens = kv_tokens;
   p.bucket_launches = 2 * (int32_t)distinct.size();
 
@@ -207,6 +222,9 @@ pkv_status build(pkv_plan& p) {
     }
     p.num_splits = S;
     p.chunk_pages = cmax;
+    // Rows of one page count share one range size, known here: the kernel
+    // can then fetch its block-table entries before the row length.
+    p.split_chunk = same_len ? cmax : 0;
     p.grid = (int32_t)grid;
     p.num_items = items;
     p.empty_items = p.grid - items;
@@ -255,6 +273,11 @@ pkv_status build(pkv_plan& p) {
     p.empty_items = fills;
   }
   p.num_slots = (int32_t)num_slots;
+  // The merge addresses one row's states with 32-bit byte offsets.
+  if (mode != PKV_MODE_UNSPLIT && (int64_t)p.num_splits * G * d * 4 > INT32_MAX) {
+    set_error("too many ranges per row (%d)", p.num_splits);
+    return PKV_ERR_INVALID;
+  }
 
   // ---- workspace layout ----
   pkv_workspace_layout& L = p.layout;

@@ -268,6 +268,35 @@ def test_fused_counters_reset_between_steps(mode):
     plan.close()
 
 
+@pytest.mark.parametrize("mode", ["split", "workqueue"])
+def test_consecutive_steps_with_new_inputs(mode):
+    """One plan and workspace, steps alternating between two different input
+    sets of the same lengths: every step's merge must read the states of
+    that step (written by workgroups on other XCDs), never an earlier one."""
+    lens = [20000, 5000, 12000, 1]
+    cases = [_mini(lens, seed=s) for s in (21, 22)]
+    devs = [W.case_to_device(c) for c in cases]
+    wants = [O.decode_case(c) for c in cases]
+    kw = dict(mode=mode, num_splits=48 if mode == "split" else 0,
+              chunk_pages=8 if mode == "workqueue" else 0)
+    _, plan, out = run_case(cases[0], devs[0], return_plan=True, **kw)
+    assert plan.stats()["grid"] >= 256
+    assert_parity(out.to(torch.float64).cpu().numpy(), wants[0], f"{mode} step 0")
+    first = [out_bits(out), None]
+    for step in range(1, 7):
+        i = step % 2
+        d = devs[i]
+        out.fill_(float("nan"))
+        plan.decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], out)
+        torch.cuda.synchronize()
+        got = out_bits(out)
+        if first[i] is None:
+            assert_parity(out.to(torch.float64).cpu().numpy(), wants[i], f"{mode} step {step}")
+            first[i] = got
+        np.testing.assert_array_equal(got, first[i])
+    plan.close()
+
+
 # --------------------------------------------- partial states on their own
 
 
