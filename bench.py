@@ -89,6 +89,31 @@ def make_inputs(name, seed, device):
     return spec, dev, case
 
 
+def to_identity_table(dev):
+    """Same cache, pages rewritten so that each sequence's pages are
+    consecutive in the pool in logical order (block table = running index):
+    the paging diagnostic (what the indirection costs against a dense
+    layout). Outputs are unchanged bit for bit."""
+    import torch
+    lens = np.asarray(dev["seq_lens_host"])
+    bt = np.asarray(dev["block_table_host"])
+    pages = (lens + 15) // 16
+    order = np.concatenate([bt[b, :pages[b]] for b in range(len(lens))]).astype(np.int64)
+    idx = torch.from_numpy(order).to(dev["k_pool"].device)
+    new_bt = np.zeros_like(bt)
+    off = 0
+    for b in range(len(lens)):
+        new_bt[b, :pages[b]] = np.arange(off, off + pages[b], dtype=np.int32)
+        off += pages[b]
+    dev = dict(dev)
+    dev["k_pool"] = dev["k_pool"].index_select(0, idx).contiguous()
+    dev["v_pool"] = dev["v_pool"].index_select(0, idx).contiguous()
+    dev["block_table"] = torch.from_numpy(new_bt).to(idx.device)
+    dev["block_table_host"] = new_bt
+    dev["num_pages"] = int(len(order))
+    return dev
+
+
 def partial_kernel_bytes(stats, spec, batch):
     """Algorithmic bytes the partial kernel moves per launch: K/V of the exact
     tokens, q, used block-table entries, seq_lens (plus out when unsplit)."""
@@ -242,6 +267,9 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times "
                          "(reference kernel for scaling rocprof byte counters)")
+    ap.add_argument("--identity-table", action="store_true",
+                    help="paging diagnostic: the same cache with each sequence's pages "
+                         "consecutive in the pool (identity block table)")
     ap.add_argument("--sweep", action="store_true",
                     help="time a grid of (mode, splits / chunk) candidates for the "
                          "workload, one JSON line each (policy calibration)")
@@ -269,6 +297,8 @@ def main():
     seed = W.SEED_HOLDOUT if a.seed is None else a.seed
     torch.cuda.set_device(0)
     spec, dev, case = make_inputs(a.config, seed, "cuda")
+    if a.identity_table:
+        dev = to_identity_table(dev)
     mode = a.mode or spec.mode
     splits = a.splits if a.splits is not None else (spec.num_splits or 0)
     if mode != "split":
@@ -319,6 +349,7 @@ def main():
             "mode": st["mode_name"], "num_splits": st["num_splits"],
             "chunk_pages": st["chunk_pages"], "merge": a.merge, "seed": seed,
             "pool_replicas": replicas,
+            "block_table": "identity" if a.identity_table else "shuffled",
         },
         "us_per_step": round(r["step_us"], 2),
         "pct_of_peak_hbm": round(100 * gbps / PEAK_HBM_GBPS, 1),
@@ -326,6 +357,7 @@ def main():
         "wall_us_per_step": round(r["wall_us_per_step"], 2),
         "sync_wall_us_with_plan": round(r["sync_wall_us_with_plan"], 2),
         "partial_kernel_marked_us": round(r["partial_marked_us"], 2),
+        "partial_kernel_marked_p10_p90_us": [round(x, 2) for x in r["partial_marked_us_p10_p90"]],
         "roofline": {
             "kernel": "partial_kernel",
             "bound": "hbm",
