@@ -82,12 +82,22 @@ typedef enum pkv_dtype { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
  *   WORKQUEUE  1-D grid over the non-empty (sequence, KV head, range) items
  *              only, every range chunk_pages pages long (the last one of a
  *              row shorter); partial + merge.
- *   AUTO       the calibrated policy picks one of the three. */
+ *   AUTO       the calibrated policy picks one of the three.
+ *   BUCKETED   comparator, never chosen by AUTO: exact-length bucketing
+ *              (PersistentKV explainer, Methodology 1 and Results, the
+ *              launch fan-out the compact work queue avoids). The rows of
+ *              each distinct N_b form a bucket planned as if it ran alone
+ *              (ranges sized so that the bucket's items fill the CUs), with
+ *              a partial launch of its own and, with PKV_MERGE_KERNEL, a
+ *              merge launch of its own; empty rows form one more bucket
+ *              that only writes zeros. Same results as WORKQUEUE up to the
+ *              split points; meant for the ablation counters and timings. */
 typedef enum pkv_mode {
   PKV_MODE_AUTO = 0,
   PKV_MODE_UNSPLIT = 1,
   PKV_MODE_SPLIT = 2,
-  PKV_MODE_WORKQUEUE = 3
+  PKV_MODE_WORKQUEUE = 3,
+  PKV_MODE_BUCKETED = 4
 } pkv_mode;
 
 /* How split states are merged (SPLIT and WORKQUEUE modes).
@@ -139,7 +149,8 @@ typedef struct pkv_plan_stats {
                               KV head of an empty row (WORKQUEUE, slot -1) */
   int32_t num_slots;       /* partial states written and merged */
   int32_t launches;        /* kernel launches per step: 1 (unsplit, or
-                              fused merge) or 2 (separate merge kernel) */
+                              fused merge) or 2 (separate merge kernel);
+                              BUCKETED: that many per bucket */
   int32_t bucket_launches; /* launches exact-length bucketing would issue:
                               one partial + one merge per distinct N_b > 0 */
   int32_t reserved;
@@ -156,7 +167,7 @@ typedef struct pkv_plan_stats {
 } pkv_plan_stats;
 
 /* Where the partial states sit in the workspace, for inspection in tests.
- * Slot of (b, g, s): WORKQUEUE  slot_base[b] + g * S_b + s, with
+ * Slot of (b, g, s): WORKQUEUE, BUCKETED  slot_base[b] + g * S_b + s, with
  * (slot_base[b], S_b) the int32 pair at meta_offset + 8*b;
  * SPLIT  (b * Hkv + g) * S + s. Per slot: m_log2[G] (the reference maximum,
  * in log2 units of the scaled logits: m_log2 = m * log2(e)), l[G] and
@@ -166,7 +177,9 @@ typedef struct pkv_plan_stats {
  * or above it by a bounded amount represents the same state. */
 typedef struct pkv_workspace_layout {
   int64_t items_offset;  /* int32x4 {b*Hkv+g, page_begin, page_end, slot} */
-  int64_t meta_offset;   /* int32x2 per sequence (WORKQUEUE) */
+  int64_t meta_offset;   /* int32x2 per sequence (WORKQUEUE, BUCKETED);
+                            BUCKETED: then int32 per sequence, the rows of
+                            the buckets one bucket after another */
   int64_t counters_offset; /* int32 per (sequence, KV head): arrivals of the
                               current step (fused merge); 0 between steps */
   int64_t m_offset;      /* fp32 [num_slots][G] */

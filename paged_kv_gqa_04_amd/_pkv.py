@@ -33,9 +33,11 @@ PKV_MODE_AUTO = 0
 PKV_MODE_UNSPLIT = 1
 PKV_MODE_SPLIT = 2
 PKV_MODE_WORKQUEUE = 3
+PKV_MODE_BUCKETED = 4
 
 MODES = {"auto": PKV_MODE_AUTO, "unsplit": PKV_MODE_UNSPLIT,
-         "split": PKV_MODE_SPLIT, "workqueue": PKV_MODE_WORKQUEUE}
+         "split": PKV_MODE_SPLIT, "workqueue": PKV_MODE_WORKQUEUE,
+         "bucketed": PKV_MODE_BUCKETED}
 MODE_NAMES = {v: k for k, v in MODES.items()}
 DTYPES = {"f16": PKV_F16, "bf16": PKV_BF16}
 

@@ -292,6 +292,7 @@ struct MergeParams {
   const float* __restrict__ ws_l;
   const float* __restrict__ ws_acc;
   const SeqMeta* __restrict__ meta;
+  const int32_t* __restrict__ rows;  // sequences of the launch (null: 0 .. B-1)
   uint16_t* __restrict__ out;
   int32_t num_kv_heads;
   int32_t num_q_heads;
@@ -891,8 +892,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
 template <int DT, int G, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams a) {
   const int bg = blockIdx.x;
-  const int b = bg / a.num_kv_heads;
+  int b = bg / a.num_kv_heads;
   const int g = bg - b * a.num_kv_heads;
+  if (a.rows) b = a.rows[b];
   int base, count;
   if (a.mode == PKV_MODE_WORKQUEUE) {
     const SeqMeta sm = a.meta[b];
@@ -1023,27 +1025,51 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
   pp.split_chunk = p->split_chunk;
   pp.scale_log2 = s.sm_scale * kLog2e;
 
+  MergeParams mp{};
+  mp.ws_m = pp.ws_m;
+  mp.ws_l = pp.ws_l;
+  mp.ws_acc = pp.ws_acc;
+  mp.meta = (const SeqMeta*)(ws + L.meta_offset);
+  mp.out = (uint16_t*)out;
+  mp.num_kv_heads = s.num_kv_heads;
+  mp.num_q_heads = s.num_q_heads;
+  mp.group = G;
+  mp.mode = p->mode;
+  mp.num_splits = p->num_splits;
+
   hipError_t e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
-  if (p->grid > 0) {
-    lp(dim3(p->grid), stream, pp);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail("partial kernel launch", e);
-  }
-  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
-  if (p->mode != PKV_MODE_UNSPLIT && !p->fused) {
-    MergeParams mp{};
-    mp.ws_m = pp.ws_m;
-    mp.ws_l = pp.ws_l;
-    mp.ws_acc = pp.ws_acc;
-    mp.meta = (const SeqMeta*)(ws + L.meta_offset);
-    mp.out = (uint16_t*)out;
-    mp.num_kv_heads = s.num_kv_heads;
-    mp.num_q_heads = s.num_q_heads;
-    mp.group = G;
-    mp.mode = p->mode;
-    mp.num_splits = p->num_splits;
-    lm(dim3(s.batch * s.num_kv_heads), stream, mp);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail("merge kernel launch", e);
+  if (p->mode == PKV_MODE_BUCKETED) {
+    // One partial launch per exact-length bucket (its items are a work
+    // queue of their own) and, with the separate merge, one merge launch
+    // over the bucket's sequences.
+    pp.mode = PKV_MODE_WORKQUEUE;
+    mp.mode = PKV_MODE_WORKQUEUE;
+    const Item* items = pp.items;
+    const int32_t* rows = (const int32_t*)(ws + L.meta_offset + sizeof(SeqMeta) * s.batch);
+    for (const Bucket& bk : p->buckets) {
+      if (bk.item_count > 0) {
+        pp.items = items + bk.item_begin;
+        lp(dim3(bk.item_count), stream, pp);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail("partial kernel launch", e);
+      }
+      if (!p->fused && bk.row_count > 0) {
+        mp.rows = rows + bk.row_begin;
+        lm(dim3(bk.row_count * s.num_kv_heads), stream, mp);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail("merge kernel launch", e);
+      }
+    }
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  } else {
+    if (p->grid > 0) {
+      lp(dim3(p->grid), stream, pp);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail("partial kernel launch", e);
+    }
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
+    if (p->mode != PKV_MODE_UNSPLIT && !p->fused) {
+      lm(dim3(s.batch * s.num_kv_heads), stream, mp);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail("merge kernel launch", e);
+    }
   }
   if (ev2 && (e = hipEventRecord(ev2, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
   return PKV_OK;

@@ -35,6 +35,13 @@ struct SeqMeta {
   int32_t splits;     // S_b: ranges per KV head of sequence b
 };
 
+// One exact-length bucket (BUCKETED mode): its items and its rows, as
+// ranges of the plan's item and row lists.
+struct Bucket {
+  int32_t item_begin, item_count;
+  int32_t row_begin, row_count;
+};
+
 }  // namespace pkv
 
 struct pkv_plan {
@@ -62,6 +69,8 @@ struct pkv_plan {
   std::vector<int32_t> seq_lens;
   std::vector<pkv::Item> items;
   std::vector<pkv::SeqMeta> meta;
+  std::vector<int32_t> rows;            // BUCKETED: sequences, bucket by bucket
+  std::vector<pkv::Bucket> buckets;     // BUCKETED
 
   pkv_workspace_layout layout{};
 

@@ -26,6 +26,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <map>
 #include <new>
 #include <set>
 
@@ -58,23 +60,25 @@ constexpr int kMinChunkPages = 2 * kWavesPerGroup;
 
 int32_t pages_of(int32_t n) { return (int32_t)ceil_div(n, kPageTokens); }
 
-// Work items (ranges of at most c pages, per row and KV head) of the step.
-int64_t items_at(const pkv_plan& p, int64_t c) {
+// Work items (ranges of at most c pages, per row and KV head) of rows `lens`.
+int64_t items_at(const std::vector<int32_t>& lens, int32_t Hkv, int64_t c) {
   int64_t n = 0;
-  for (int32_t len : p.seq_lens) n += ceil_div(pages_of(len), c);
-  return n * p.shape.num_kv_heads;
+  for (int32_t len : lens) n += ceil_div(pages_of(len), c);
+  return n * Hkv;
 }
 
-// Range size: the smallest multiple of the wave count, from the even share
-// of the step's page-heads per CU up to kMaxChunkPages, whose items (each
-// row rounded up separately) fit one per CU.
-int32_t auto_chunk(const pkv_plan& p, int64_t total_pages) {
-  const int64_t target = std::max<int64_t>(1, (int64_t)p.num_cus * kTargetItemsPerCU);
-  const int64_t work = total_pages * p.shape.num_kv_heads;
+// Range size for rows `lens`: the smallest multiple of the wave count, from
+// the even share of their page-heads per CU up to kMaxChunkPages, whose
+// items (each row rounded up separately) fit one per CU.
+int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t Hkv, int32_t num_cus) {
+  const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * kTargetItemsPerCU);
+  int64_t total_pages = 0;
+  for (int32_t len : lens) total_pages += pages_of(len);
+  const int64_t work = total_pages * Hkv;
   int64_t c = std::min<int64_t>(std::max<int64_t>(ceil_div(work, target), kMinChunkPages),
                                 kMaxChunkPages);
   c = align_up(c, kWavesPerGroup);
-  while (c < kMaxChunkPages && items_at(p, c) > target) c += kWavesPerGroup;
+  while (c < kMaxChunkPages && items_at(lens, Hkv, c) > target) c += kWavesPerGroup;
   return (int32_t)c;
 }
 
@@ -163,7 +167,7 @@ pkv_status build(pkv_plan& p) {
 
   // ---- mode ----
   int32_t mode = p.opts.mode;
-  if (mode < PKV_MODE_AUTO || mode > PKV_MODE_WORKQUEUE) {
+  if (mode < PKV_MODE_AUTO || mode > PKV_MODE_BUCKETED) {
     set_error("unknown mode %d", mode);
     return PKV_ERR_INVALID;
   }
@@ -176,7 +180,8 @@ pkv_status build(pkv_plan& p) {
     return PKV_ERR_INVALID;
   }
   p.fused = p.opts.merge == PKV_MERGE_FUSED;
-  int32_t chunk = p.opts.chunk_pages > 0 ? p.opts.chunk_pages : auto_chunk(p, total_pages);
+  int32_t chunk = p.opts.chunk_pages > 0 ? p.opts.chunk_pages
+                                         : auto_chunk(p.seq_lens, Hkv, p.num_cus);
   if (mode == PKV_MODE_AUTO) {
     if (active == 0 || max_pages <= chunk) {
       mode = PKV_MODE_UNSPLIT;  // every row fits in one item: nothing to merge
@@ -189,6 +194,8 @@ pkv_status build(pkv_plan& p) {
 
   p.items.clear();
   p.meta.clear();
+  p.rows.clear();
+  p.buckets.clear();
   p.mode = mode;
   p.split_chunk = 0;
   p.kv_tokens = kv_tokens;
@@ -229,6 +236,51 @@ pkv_status build(pkv_plan& p) {
     p.num_items = items;
     p.empty_items = p.grid - items;
     num_slots = grid;
+  } else if (mode == PKV_MODE_BUCKETED) {
+    // Exact-length buckets, longest first; empty rows last, as a bucket
+    // that only writes zeros.
+    std::map<int32_t, std::vector<int32_t>, std::greater<int32_t>> by_len;
+    for (int32_t b = 0; b < B; ++b) by_len[p.seq_lens[b]].push_back(b);
+    p.meta.assign(B, SeqMeta{0, 0});
+    int32_t smax = 0, cmax = 0, fills = 0;
+    for (const auto& kv : by_len) {
+      const int32_t len = kv.first, pg = pages_of(len);
+      const std::vector<int32_t>& rows = kv.second;
+      Bucket bk{(int32_t)p.items.size(), 0, (int32_t)p.rows.size(), (int32_t)rows.size()};
+      if (pg > 0) {
+        // Planned as if the bucket ran alone: its own range size.
+        const std::vector<int32_t> lens(rows.size(), len);
+        const int32_t c = p.opts.chunk_pages > 0 ? p.opts.chunk_pages
+                                                 : auto_chunk(lens, Hkv, p.num_cus);
+        const int32_t Sb = (int32_t)ceil_div(pg, c);
+        for (int32_t b : rows) {
+          p.meta[b] = {(int32_t)num_slots, Sb};
+          for (int32_t g = 0; g < Hkv; ++g)
+            for (int32_t si = 0; si < Sb; ++si)
+              p.items.push_back({b * Hkv + g, si * c, std::min(pg, (si + 1) * c),
+                                 (int32_t)(num_slots + (int64_t)g * Sb + si)});
+          num_slots += (int64_t)Hkv * Sb;
+          if (num_slots > INT32_MAX / 2) {
+            set_error("bucket plan too large");
+            return PKV_ERR_INVALID;
+          }
+        }
+        smax = std::max(smax, Sb);
+        cmax = std::max(cmax, c);
+      } else if (p.fused) {
+        for (int32_t b : rows)
+          for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1});
+        fills += (int32_t)rows.size() * Hkv;
+      }
+      for (int32_t b : rows) p.rows.push_back(b);
+      bk.item_count = (int32_t)p.items.size() - bk.item_begin;
+      p.buckets.push_back(bk);
+    }
+    p.num_splits = std::max(smax, 1);
+    p.chunk_pages = cmax;
+    p.grid = (int32_t)p.items.size();
+    p.num_items = p.grid - fills;
+    p.empty_items = fills;
   } else {  // WORKQUEUE
     if (chunk <= 0) chunk = kMinChunkPages;
     int32_t smax = 0;
@@ -286,7 +338,9 @@ pkv_status build(pkv_plan& p) {
   L.items_offset = off;
   off = align_up(off + (int64_t)p.items.size() * (int64_t)sizeof(Item), kAlign);
   L.meta_offset = off;
-  off = align_up(off + (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta), kAlign);
+  const int64_t meta_end =
+      off + (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta) + (int64_t)p.rows.size() * 4;
+  off = align_up(meta_end, kAlign);
   L.counters_offset = off;
   const bool counters = mode != PKV_MODE_UNSPLIT && p.fused;
   const int64_t counters_end = off + (counters ? (int64_t)B * Hkv * 4 : 0);
@@ -314,8 +368,8 @@ pkv_status build(pkv_plan& p) {
     p.upload_bytes = 0;
   else if (counters)
     p.upload_bytes = counters_end;
-  else if (mode == PKV_MODE_WORKQUEUE)
-    p.upload_bytes = L.meta_offset + (int64_t)p.meta.size() * (int64_t)sizeof(SeqMeta);
+  else if (mode == PKV_MODE_WORKQUEUE || mode == PKV_MODE_BUCKETED)
+    p.upload_bytes = meta_end;
   else
     p.upload_bytes = 0;
   p.uploaded = false;
@@ -331,6 +385,9 @@ void write_upload_image(const pkv_plan& p, void* dst) {
     std::memcpy(d + p.layout.items_offset, p.items.data(), p.items.size() * sizeof(Item));
   if (!p.meta.empty())
     std::memcpy(d + p.layout.meta_offset, p.meta.data(), p.meta.size() * sizeof(SeqMeta));
+  if (!p.rows.empty())
+    std::memcpy(d + p.layout.meta_offset + p.meta.size() * sizeof(SeqMeta), p.rows.data(),
+                p.rows.size() * sizeof(int32_t));
 }
 
 void set_error(const char* fmt, ...) {
@@ -416,7 +473,8 @@ pkv_status pkv_plan_stats_get(const pkv_plan* p, pkv_plan_stats* s) {
   s->num_items = p->num_items;
   s->empty_items = p->empty_items;
   s->num_slots = p->num_slots;
-  s->launches = (p->mode == PKV_MODE_UNSPLIT || p->fused) ? 1 : 2;
+  const int32_t per = (p->mode == PKV_MODE_UNSPLIT || p->fused) ? 1 : 2;
+  s->launches = p->mode == PKV_MODE_BUCKETED ? per * (int32_t)p->buckets.size() : per;
   s->bucket_launches = p->bucket_launches;
   s->kv_tokens = p->kv_tokens;
   s->algorithmic_bytes = p->algorithmic_bytes;

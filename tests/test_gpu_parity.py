@@ -61,7 +61,8 @@ def mixed_case():
 
 
 @pytest.mark.parametrize("mode,chunk", [("workqueue", 0), ("auto", 0), ("split", 0),
-                                        ("unsplit", 0), ("workqueue", 5), ("workqueue", 64)])
+                                        ("unsplit", 0), ("workqueue", 5), ("workqueue", 64),
+                                        ("bucketed", 0)])
 def test_mixed8(mixed_case, mode, chunk):
     c, dev, want = mixed_case
     got = run_case(c, dev, mode=mode, chunk_pages=chunk)
@@ -73,6 +74,27 @@ def test_b4(mode):
     c = W.make_case("b4")
     got = run_case(c, mode=mode)
     assert_parity(got, O.decode_case(c), f"b4/{mode}")
+
+
+_TRACE_CACHE = {}
+
+
+def _trace_case(name):
+    if name not in _TRACE_CACHE:
+        c = W.make_case(name)  # hold-out seed; unowned pool pages poisoned
+        _TRACE_CACHE.clear()  # keep one case (and its oracle) in memory
+        _TRACE_CACHE[name] = (c, W.case_to_device(c), O.decode_case(c))
+    return _TRACE_CACHE[name]
+
+
+@pytest.mark.parametrize("mode", ["auto", "bucketed", "split"])
+@pytest.mark.parametrize("name", ["bucketed1"] + list(W.TRACE_FAMILIES))
+def test_trace_families(name, mode):
+    """The Bucketed / Bimodal / Uniform / Zipf-like traces in the policy's
+    choice, exact-length bucketing and the rectangular split grid."""
+    c, dev, want = _trace_case(name)
+    assert_parity(run_case(c, dev, mode=mode, merge="kernel" if mode == "bucketed" else "fused"),
+                  want, f"{name}/{mode}")
 
 
 @pytest.mark.slow
@@ -120,12 +142,12 @@ def test_split_count_changes_only_rounding():
 @pytest.mark.parametrize("dtype", [W.BF16, W.F16])
 @pytest.mark.parametrize("G,Hkv,d", [(1, 4, 128), (2, 2, 64), (4, 1, 64), (8, 2, 128), (8, 1, 64),
                                      (4, 3, 128), (1, 1, 64)])
-@pytest.mark.parametrize("mode", ["unsplit", "split", "workqueue"])
+@pytest.mark.parametrize("mode", ["unsplit", "split", "workqueue", "bucketed"])
 def test_shapes_and_ragged_tails(dtype, G, Hkv, d, mode):
     lens = [0, 1, 15, 16, 17, 33, 255, 1000]
     c = _mini(lens, G=G, Hkv=Hkv, d=d, dtype=dtype, seed=G * 100 + Hkv * 10 + d)
     got = run_case(c, mode=mode, num_splits=3 if mode == "split" else 0,
-                   chunk_pages=2 if mode == "workqueue" else 0)
+                   chunk_pages=2 if mode in ("workqueue", "bucketed") else 0)
     want = O.decode_case(c)
     assert_parity(got, want, f"{dtype}/G{G}/Hkv{Hkv}/d{d}/{mode}")
     assert (got[0] == 0).all()  # empty row -> zeros
@@ -233,14 +255,17 @@ def test_repeated_runs_bitwise():
 # ------------------------------------------------------ merge placement
 
 
-@pytest.mark.parametrize("mode", ["split", "workqueue"])
+@pytest.mark.parametrize("mode", ["split", "workqueue", "bucketed"])
 def test_fused_and_kernel_merge_give_identical_bits(mode):
     c = _mini([3000, 17, 0, 900, 4100], seed=12)
     kw = dict(mode=mode, num_splits=6 if mode == "split" else 0,
               chunk_pages=5 if mode == "workqueue" else 0, return_plan=True)
     _, pf, of = run_case(c, merge="fused", **kw)
     _, pk, ok = run_case(c, merge="kernel", **kw)
-    assert pf.stats()["launches"] == 1 and pk.stats()["launches"] == 2
+    if mode != "bucketed":
+        assert pf.stats()["launches"] == 1 and pk.stats()["launches"] == 2
+    else:  # 4 distinct lengths and an empty row: 5 buckets
+        assert pf.stats()["launches"] == 5 and pk.stats()["launches"] == 10
     np.testing.assert_array_equal(out_bits(of), out_bits(ok))
     assert_parity(of.to(torch.float64).cpu().numpy(), O.decode_case(c), f"fused/{mode}")
     pf.close()

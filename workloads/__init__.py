@@ -52,6 +52,8 @@ class ConfigSpec:
     head_dim: int
     dtype: str
     lengths: tuple  # ("fixed", n) | ("uniform", lo, hi) | ("loguniform", lo, hi)
+    #                 | ("bucketed", n1, n2, ...) | ("bimodal", lo1, hi1, lo2, hi2, p)
+    #                 | ("zipf", unit, kmax, a)
     pool_pages: int | None = None  # None: exactly the pages the batch uses
     num_splits: int | None = None  # S named by the workload, if any
     mode: str = "auto"  # the dispatch mode the workload is quoted in
@@ -92,7 +94,34 @@ CONFIGS: dict[str, ConfigSpec] = {
         description="B=64, Hq=64, Hkv=8 (G=8), d=128, bf16, lengths "
                     "log-uniform in [4096, 131072], work queue",
     ),
+    # Trace families of the PersistentKV explainer (Evaluation protocol,
+    # traces isolating context length, active batch size and raggedness).
+    # The pages give no parameters; these are plain readings of the names.
+    "bucketed1": ConfigSpec(
+        "bucketed1", 6, 1, 32, 8, 128, BF16, ("bucketed", 8192, 16384, 32768, 65536),
+        mode="auto",
+        description="B=1, Hq=32, Hkv=8, d=128, bf16, length drawn from the "
+                    "power-of-two buckets {8192, 16384, 32768, 65536}",
+    ),
+    "bimodal8": ConfigSpec(
+        "bimodal8", 7, 8, 32, 8, 128, BF16, ("bimodal", 256, 1024, 16384, 32768, 0.5),
+        mode="auto",
+        description="B=8, Hq=32, Hkv=8, d=128, bf16, lengths short U[256, 1024] or "
+                    "long U[16384, 32768] with probability 1/2 each",
+    ),
+    "uniform8": ConfigSpec(
+        "uniform8", 8, 8, 32, 8, 128, BF16, ("uniform", 256, 32768), mode="auto",
+        description="B=8, Hq=32, Hkv=8, d=128, bf16, lengths uniform in [256, 32768]",
+    ),
+    "zipf8": ConfigSpec(
+        "zipf8", 9, 8, 32, 8, 128, BF16, ("zipf", 256, 128, 1.1), mode="auto",
+        description="B=8, Hq=32, Hkv=8, d=128, bf16, lengths 256 k with k in 1..128 "
+                    "drawn with probability proportional to k^-1.1 (Zipf-like)",
+    ),
 }
+
+# The B=8 trace families, in the order the pages list them.
+TRACE_FAMILIES = ("bimodal8", "uniform8", "zipf8")
 
 
 def pages_for(n: int, page: int = PAGE_TOKENS) -> int:
@@ -104,7 +133,12 @@ def draw_lengths(lengths: tuple, batch: int, rng: np.random.Generator) -> np.nda
 
     * fixed: every row has ``n`` tokens;
     * uniform: integers in ``[lo, hi]`` inclusive;
-    * loguniform: ``clip(round(exp(U(ln lo, ln hi))), lo, hi)``.
+    * loguniform: ``clip(round(exp(U(ln lo, ln hi))), lo, hi)``;
+    * bucketed: each row takes one of the listed values, uniformly;
+    * bimodal: with probability ``p`` uniform in ``[lo1, hi1]``, else in
+      ``[lo2, hi2]``;
+    * zipf: ``unit * k`` with ``k`` in ``1..kmax``, ``P(k)`` proportional to
+      ``k^-a`` (inverse-CDF draw from one uniform per row).
     """
     kind = lengths[0]
     if kind == "fixed":
@@ -116,6 +150,21 @@ def draw_lengths(lengths: tuple, batch: int, rng: np.random.Generator) -> np.nda
         lo, hi = int(lengths[1]), int(lengths[2])
         u = rng.uniform(math.log(lo), math.log(hi), size=batch)
         return np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int32)
+    if kind == "bucketed":
+        values = np.asarray(lengths[1:], dtype=np.int64)
+        return values[rng.integers(0, len(values), size=batch)].astype(np.int32)
+    if kind == "bimodal":
+        lo1, hi1, lo2, hi2, p = lengths[1:]
+        first = rng.uniform(size=batch) < float(p)
+        a = rng.integers(int(lo1), int(hi1) + 1, size=batch)
+        b = rng.integers(int(lo2), int(hi2) + 1, size=batch)
+        return np.where(first, a, b).astype(np.int32)
+    if kind == "zipf":
+        unit, kmax, a = int(lengths[1]), int(lengths[2]), float(lengths[3])
+        w = np.arange(1, kmax + 1, dtype=np.float64) ** -a
+        cdf = np.cumsum(w) / w.sum()
+        k = np.searchsorted(cdf, rng.uniform(size=batch), side="right") + 1
+        return (unit * np.minimum(k, kmax)).astype(np.int32)
     raise ValueError(f"unknown length distribution {kind!r}")
 
 
