@@ -13,6 +13,8 @@ of the pools (so each copy is evicted by the others before it is read again).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
                        [--mode split] [--splits 32] [--chunk 0] [--no-cpu]
+                       [--merge fused|kernel] [--seed N] [--identity-table]
+       python bench.py --config mixed8 --sweep | --ablation   (one line per candidate)
 """
 
 from __future__ import annotations
@@ -230,6 +232,30 @@ def sweep(P, dev, spec, replicas, ev, a):
         }), flush=True)
 
 
+def ablation(P, dev, spec, replicas, ev, a):
+    """The scheduling comparators of the PersistentKV explainer (Results,
+    scheduling overhead) on one workload: the policy's choice, the unsplit
+    path, the rectangular split grid, the compact work queue and
+    exact-length bucketing (the last two also with the pages' separate merge
+    launch). One JSON line each, with the scheduler counters."""
+    cands = [("auto", "fused"), ("unsplit", "fused"), ("split", "fused"), ("split", "kernel"),
+             ("workqueue", "fused"), ("workqueue", "kernel"), ("bucketed", "fused"),
+             ("bucketed", "kernel")]
+    for mode, merge in cands:
+        r = time_mode(P, dev, spec, mode, 0, 0, a.steps, a.warmup, replicas, ev, merge)
+        st = r["stats"]
+        print(json.dumps({
+            "workload": spec.name, "seed": a.seed, "mode": mode, "merge": merge,
+            "resolved": st["mode_name"], "num_splits": st["num_splits"],
+            "chunk_pages": st["chunk_pages"], "grid": st["grid"],
+            "launches": st["launches"], "bucket_launches": st["bucket_launches"],
+            "num_slots": st["num_slots"], "partial_bytes": st["partial_bytes"],
+            "us_per_step": round(r["step_us"], 2),
+            "gbps": round(st["algorithmic_bytes"] / (r["step_us"] * 1e-6) / 1e9, 1),
+            "sync_wall_us_with_plan": round(r["sync_wall_us_with_plan"], 2),
+        }), flush=True)
+
+
 def cpu_baseline(case, target_s=10.0, cap_s=30.0):
     """Time the CPU oracle on the bench workload until ~target_s of work."""
     from oracle import paged_gqa as O
@@ -270,6 +296,9 @@ def main():
     ap.add_argument("--identity-table", action="store_true",
                     help="paging diagnostic: the same cache with each sequence's pages "
                          "consecutive in the pool (identity block table)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time the scheduling comparators (unsplit, rectangular split, "
+                         "work queue, exact-length bucketing), one JSON line each")
     ap.add_argument("--sweep", action="store_true",
                     help="time a grid of (mode, splits / chunk) candidates for the "
                          "workload, one JSON line each (policy calibration)")
@@ -315,6 +344,9 @@ def main():
 
     if a.sweep:
         sweep(P, dev, spec, replicas, ev, a)
+        return
+    if a.ablation:
+        ablation(P, dev, spec, replicas, ev, a)
         return
     r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev, a.merge)
     st = r["stats"]
