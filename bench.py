@@ -256,6 +256,40 @@ def ablation(P, dev, spec, replicas, ev, a):
         }), flush=True)
 
 
+def time_append(P, dev, spec, steps, warmup, ev):
+    """Time the append step (the new token's K/V of every row written through
+    the block table) as `steps` back-to-back launches. Each row rewrites its
+    last token (position N_b - 1, a page the table already holds), so every
+    launch does the full work without growing the cache."""
+    import torch
+    lens = np.asarray(dev["seq_lens_host"])
+    B, Hkv, d = len(lens), spec.num_kv_heads, spec.head_dim
+    td = dev["k_pool"].dtype
+    g = torch.Generator(device=dev["k_pool"].device).manual_seed(1)
+    k_new = torch.randn((B, Hkv, d), generator=g, device=dev["k_pool"].device).to(td)
+    v_new = torch.randn((B, Hkv, d), generator=g, device=dev["k_pool"].device).to(td)
+    pos = torch.from_numpy(np.maximum(lens - 1, 0).astype(np.int32)).to(k_new.device)
+    shape = P.make_shape(B, spec.num_q_heads, Hkv, d, dev["block_table_host"].shape[1],
+                         dev["num_pages"], spec.dtype)
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (k_new, v_new, dev["k_pool"], dev["v_pool"], dev["block_table"], pos)
+    for _ in range(warmup):
+        P.pkv_append(shape, *args, None, stream)
+    torch.cuda.synchronize()
+    e = ev.create(2)
+    ev.record(e[0], stream)
+    for _ in range(steps):
+        P.pkv_append(shape, *args, None, stream)
+    ev.record(e[1], stream)
+    torch.cuda.synchronize()
+    us = ev.ms(e[0], e[1]) / steps * 1e3
+    ev.destroy(e)
+    # new K/V read + written, plus one table entry and one length per row
+    nbytes = 2 * 2 * B * Hkv * d * 2 + 8 * B
+    return {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes),
+            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1), "rows": int(B)}
+
+
 def cpu_baseline(case, target_s=10.0, cap_s=30.0):
     """Time the CPU oracle on the bench workload until ~target_s of work."""
     from oracle import paged_gqa as O
@@ -296,6 +330,9 @@ def main():
     ap.add_argument("--identity-table", action="store_true",
                     help="paging diagnostic: the same cache with each sequence's pages "
                          "consecutive in the pool (identity block table)")
+    ap.add_argument("--append", action="store_true",
+                    help="also time the append step (new-token K/V written through "
+                         "the block table) on the workload")
     ap.add_argument("--ablation", action="store_true",
                     help="time the scheduling comparators (unsplit, rectangular split, "
                          "work queue, exact-length bucketing), one JSON line each")
@@ -415,6 +452,8 @@ def main():
             "us_per_step": round(ra["step_us"], 2),
             "gbps": round(sa["algorithmic_bytes"] / (ra["step_us"] * 1e-6) / 1e9, 1),
         }
+    if a.append:
+        line["append"] = time_append(P, dev, spec, a.steps, a.warmup, ev)
     if not a.no_cpu and case is not None:
         sec, reps_done, threads = cpu_baseline(case)
         line["cpu_baseline"] = {

@@ -67,7 +67,8 @@ typedef enum pkv_status {
   PKV_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, G, page size */
   PKV_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
   PKV_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
-  PKV_ERR_STATE = -5        /* call out of order (e.g. decode before upload) */
+  PKV_ERR_STATE = -5,       /* call out of order (e.g. decode before upload) */
+  PKV_ERR_POOL = -6         /* page pool exhausted (nothing was taken) */
 } pkv_status;
 
 /* Storage dtype shared by q, the K/V pools and out. */
@@ -265,6 +266,74 @@ pkv_status pkv_decode_marked(const pkv_plan* plan, const void* q,
 
 /* Free a plan (NULL is a no-op). Waits for its last upload copy. */
 void pkv_plan_destroy(pkv_plan* plan);
+
+/* ---------------------------------------------------------------------------
+ * Paged KV append: the step before decode. Each sequence keeps its cache in
+ * fixed-size pages of one shared pool; a sequence takes a new page from the
+ * pool when its tail page is full, and a finished sequence's pages go back
+ * to the pool at once, for other sequences to reuse (ZimaSpace post, on
+ * fixed-size blocks and on blocks released when a request ends; ai-trend
+ * study note, "How it works", steps two and four). The token at logical
+ * position t of sequence b lives at (block_table[b][t / P], g, t % P).
+ * ------------------------------------------------------------------------- */
+
+typedef struct pkv_pool pkv_pool; /* opaque host-side page allocator */
+
+/* A free list over pool pages 0 .. num_pages-1, all free at creation; pages
+ * are handed out lowest index first, and freed pages are reused first (last
+ * in, first out). Host only. Errors: PKV_ERR_INVALID (num_pages <= 0, null). */
+pkv_status pkv_pool_create(int32_t num_pages, pkv_pool** out_pool);
+
+/* Free the allocator (NULL is a no-op). */
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Pages currently free (-1 for a NULL pool). */
+int32_t pkv_pool_free_pages(const pkv_pool* pool);
+
+/* Take n pages into pages[0 .. n-1]. Errors: PKV_ERR_POOL when fewer than n
+ * are free (nothing taken), PKV_ERR_INVALID (n < 0, null). */
+pkv_status pkv_pool_alloc(pkv_pool* pool, int32_t n, int32_t* pages);
+
+/* Return n pages. Errors: PKV_ERR_INVALID, with nothing returned, if a page
+ * is outside the pool, not currently taken, or listed twice. */
+pkv_status pkv_pool_free(pkv_pool* pool, const int32_t* pages, int32_t n);
+
+/* Host half of one append step for a batch: row b's new token goes to
+ * position N_b = seq_lens_host[b]; a row whose position opens a page
+ * (N_b % page_size == 0) takes a page from the pool into
+ * block_table_host[b * stride + N_b / page_size]. *pages_taken (may be NULL)
+ * receives how many pages were taken. Errors: PKV_ERR_INVALID (null, N_b < 0,
+ * position past the table row: N_b >= stride * page_size); PKV_ERR_POOL
+ * (pool exhausted). On any error nothing is taken and the table is
+ * unchanged. */
+pkv_status pkv_append_prepare(pkv_pool* pool, int32_t batch, int32_t block_table_stride,
+                              int32_t page_size, const int32_t* seq_lens_host,
+                              int32_t* block_table_host, int32_t* pages_taken);
+
+/* A sequence has finished: return the pages of its first
+ * ceil(seq_len / page_size) table entries to the pool and set those entries
+ * to -1. Errors as pkv_pool_free (then nothing is returned and the row is
+ * unchanged). Pages shared with another row must not be released while that
+ * row still uses them (the allocator keeps no reference counts). */
+pkv_status pkv_pool_release_row(pkv_pool* pool, int32_t* block_table_row, int32_t seq_len,
+                                int32_t page_size);
+
+/* Device half: write every row's new token on `stream` (asynchronous).
+ *   shape        batch, num_kv_heads, head_dim, page_size,
+ *                block_table_stride, num_pages and dtype are used.
+ *   k_new, v_new device [batch, Hkv, d] in the shape's dtype, 4-byte aligned.
+ *   k_pool, v_pool  device [num_pages, Hkv, page_size, d].
+ *   block_table  device int32 [batch, stride]; seq_lens device int32 [batch]:
+ *                each row's position (its length before the append).
+ *   new_seq_lens device int32 [batch] or NULL: receives seq_lens[b] + 1; it
+ *                must not alias seq_lens.
+ * A row whose position is negative or past the table row, or whose page
+ * entry is outside [0, num_pages), writes no K/V (new_seq_lens still gets
+ * seq_lens[b] + 1). Errors: PKV_ERR_INVALID (null or misaligned pointer, bad
+ * shape), PKV_ERR_UNSUPPORTED (head_dim, page size, dtype), PKV_ERR_HIP. */
+pkv_status pkv_append(const pkv_shape* shape, const void* k_new, const void* v_new,
+                      void* k_pool, void* v_pool, const int32_t* block_table,
+                      const int32_t* seq_lens, int32_t* new_seq_lens, hipStream_t stream);
 
 /* Static string naming a status code. */
 const char* pkv_status_string(int32_t status);

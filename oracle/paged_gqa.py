@@ -33,6 +33,12 @@ Computation is the plain definition: gather, exact two-pass softmax in float64
 library primitive. Stored fp16 / bf16 bits are widened exactly, so no
 rounding happens before accumulation.
 
+``append_tokens`` is the step before decode: every sequence's new token is
+stored at its next logical position ``N_b``, i.e. slot ``N_b % P`` of page
+``block_table[b, N_b // P]`` (the same mapping; ZimaSpace post, fixed-size
+blocks: a sequence takes further blocks from the shared pool as tokens
+arrive). The oracle writes raw storage bits into copies of the pools.
+
 ``range_state`` and ``merge_states`` restate the split form from the same
 page (Methodology 1, sequence splitting): the sequence axis is cut into
 disjoint ranges, each summarised by a partial online-softmax state
@@ -160,3 +166,25 @@ def merge_states(states) -> np.ndarray:
         w = np.where(ms[:, h] == -np.inf, 0.0, np.exp(ms[:, h] - M[h]))
         out[h] = (w[:, None] * accs[:, h, :]).sum(axis=0) / (w * ls[:, h]).sum()
     return out
+
+
+def append_tokens(k_pool, v_pool, block_table, seq_lens, k_new, v_new, page=16):
+    """Pools after one append step, as new arrays (inputs unchanged).
+
+    Row ``b`` stores ``k_new[b]`` / ``v_new[b]`` (raw bits, [Hkv, d]) as its
+    logical token ``N_b = seq_lens[b]``: page ``block_table[b, N_b // page]``,
+    slot ``N_b % page``, every KV head. A row whose table entry is outside
+    the pool stores nothing (the kernels' rule for untrusted entries).
+    """
+    k = np.array(k_pool, copy=True)
+    v = np.array(v_pool, copy=True)
+    for b, n in enumerate(np.asarray(seq_lens)):
+        n = int(n)
+        if n < 0 or n // page >= block_table.shape[1]:
+            continue
+        pg = int(block_table[b, n // page])
+        if not 0 <= pg < k.shape[0]:
+            continue
+        k[pg, :, n % page, :] = k_new[b]
+        v[pg, :, n % page, :] = v_new[b]
+    return k, v

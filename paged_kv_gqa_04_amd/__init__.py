@@ -17,6 +17,7 @@ from ._pkv import (  # noqa: F401
     PKV_BF16,
     PKV_ERR_HIP,
     PKV_ERR_INVALID,
+    PKV_ERR_POOL,
     PKV_ERR_STATE,
     PKV_ERR_UNSUPPORTED,
     PKV_ERR_WORKSPACE,
@@ -26,11 +27,14 @@ from ._pkv import (  # noqa: F401
     PKV_MODE_AUTO,
     PKV_MODE_SPLIT,
     PKV_MODE_UNSPLIT,
+    PKV_MODE_BUCKETED,
     PKV_MODE_WORKQUEUE,
     PKV_OK,
     PkvError,
     make_opts,
     make_shape,
+    pkv_append,
+    pkv_append_prepare,
     pkv_decode,
     pkv_decode_marked,
     pkv_last_error,
@@ -42,6 +46,12 @@ from ._pkv import (  # noqa: F401
     pkv_plan_update,
     pkv_plan_upload,
     pkv_plan_workspace_bytes,
+    pkv_pool_alloc,
+    pkv_pool_create,
+    pkv_pool_destroy,
+    pkv_pool_free,
+    pkv_pool_free_pages,
+    pkv_pool_release_row,
     pkv_status_string,
     pkv_version,
 )
@@ -123,3 +133,42 @@ def decode_step(q, k_pool, v_pool, block_table, seq_lens, seq_lens_host, *,
         stats = plan.stats()
         torch.cuda.current_stream().synchronize()
     return out, stats
+
+
+class Pool:
+    """Host page allocator over a pool of ``num_pages`` pages (see pkv.h)."""
+
+    def __init__(self, num_pages: int):
+        self.handle = pkv_pool_create(num_pages)
+
+    def free_pages(self) -> int:
+        return pkv_pool_free_pages(self.handle)
+
+    def alloc(self, n: int):
+        return pkv_pool_alloc(self.handle, n)
+
+    def free(self, pages) -> None:
+        pkv_pool_free(self.handle, pages)
+
+    def prepare(self, seq_lens_host, block_table_host, page_size: int = 16) -> int:
+        return pkv_append_prepare(self.handle, seq_lens_host, block_table_host, page_size)
+
+    def release_row(self, block_table_row, seq_len: int, page_size: int = 16) -> None:
+        pkv_pool_release_row(self.handle, block_table_row, seq_len, page_size)
+
+    def close(self) -> None:
+        if self.handle:
+            pkv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover
+            pass

@@ -25,6 +25,7 @@ PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
 PKV_ERR_STATE = -5
+PKV_ERR_POOL = -6
 
 PKV_F16 = 0
 PKV_BF16 = 1
@@ -97,6 +98,16 @@ SIGNATURES = {
     "pkv_status_string": (C.c_char_p, [C.c_int32]),
     "pkv_last_error": (C.c_char_p, []),
     "pkv_version": (C.c_int32, []),
+    "pkv_pool_create": (C.c_int32, [C.c_int32, C.POINTER(_P)]),
+    "pkv_pool_destroy": (None, [_P]),
+    "pkv_pool_free_pages": (C.c_int32, [_P]),
+    "pkv_pool_alloc": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_int32)]),
+    "pkv_pool_free": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "pkv_append_prepare": (C.c_int32, [_P, C.c_int32, C.c_int32, C.c_int32,
+                                       C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                       C.POINTER(C.c_int32)]),
+    "pkv_pool_release_row": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32, C.c_int32]),
+    "pkv_append": (C.c_int32, [C.POINTER(pkv_shape), _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -250,3 +261,70 @@ def pkv_last_error() -> str:
 
 def pkv_version() -> int:
     return int(LIB.pkv_version())
+
+
+# ------------------------------------------------------------- KV append
+
+
+def _i32(arr):
+    """A writable contiguous int32 numpy view and its ctypes pointer."""
+    a = np.ascontiguousarray(arr, dtype=np.int32)
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def pkv_pool_create(num_pages: int) -> int:
+    h = C.c_void_p()
+    _check(LIB.pkv_pool_create(int(num_pages), C.byref(h)), "pkv_pool_create")
+    return h.value
+
+
+def pkv_pool_destroy(pool: int) -> None:
+    if pool:
+        LIB.pkv_pool_destroy(pool)
+
+
+def pkv_pool_free_pages(pool: int) -> int:
+    return int(LIB.pkv_pool_free_pages(pool))
+
+
+def pkv_pool_alloc(pool: int, n: int) -> np.ndarray:
+    out, ptr = _i32(np.zeros(max(int(n), 1), dtype=np.int32))
+    _check(LIB.pkv_pool_alloc(pool, int(n), ptr), "pkv_pool_alloc")
+    return out[:int(n)].copy()
+
+
+def pkv_pool_free(pool: int, pages) -> None:
+    a, ptr = _i32(pages)
+    _check(LIB.pkv_pool_free(pool, ptr, int(a.size)), "pkv_pool_free")
+
+
+def pkv_append_prepare(pool: int, seq_lens_host, block_table_host: np.ndarray,
+                       page_size: int = 16) -> int:
+    """Host half of an append step; updates ``block_table_host`` (int32
+    [B, stride], C-contiguous) in place and returns the pages taken."""
+    if block_table_host.dtype != np.int32 or not block_table_host.flags.c_contiguous:
+        raise ValueError("block_table_host must be a C-contiguous int32 array")
+    lens, lp = _i32(seq_lens_host)
+    taken = C.c_int32(0)
+    _check(LIB.pkv_append_prepare(pool, int(lens.size), int(block_table_host.shape[1]),
+                                  int(page_size), lp,
+                                  block_table_host.ctypes.data_as(C.POINTER(C.c_int32)),
+                                  C.byref(taken)), "pkv_append_prepare")
+    return int(taken.value)
+
+
+def pkv_pool_release_row(pool: int, block_table_row: np.ndarray, seq_len: int,
+                         page_size: int = 16) -> None:
+    """Return a finished row's pages; ``block_table_row`` (int32, contiguous)
+    is updated in place (entries set to -1)."""
+    if block_table_row.dtype != np.int32 or not block_table_row.flags.c_contiguous:
+        raise ValueError("block_table_row must be a C-contiguous int32 array")
+    _check(LIB.pkv_pool_release_row(pool, block_table_row.ctypes.data_as(C.POINTER(C.c_int32)),
+                                    int(seq_len), int(page_size)), "pkv_pool_release_row")
+
+
+def pkv_append(shape: pkv_shape, k_new, v_new, k_pool, v_pool, block_table, seq_lens,
+               new_seq_lens=None, stream=0) -> None:
+    _check(LIB.pkv_append(C.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                          _ptr(block_table), _ptr(seq_lens), _ptr(new_seq_lens),
+                          _ptr(stream) or None), "pkv_append")

@@ -20,8 +20,8 @@ LIB_NAME = "libpkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-HOST_SOURCES = ["plan.cpp"]  # plain C++, built by the host compiler
-HIP_SOURCES = ["decode.hip"]
+HOST_SOURCES = ["plan.cpp", "pool.cpp"]  # plain C++, built by the host compiler
+HIP_SOURCES = ["decode.hip", "append.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
               "-I", os.path.join(ROCM, "include")]

@@ -524,6 +524,7 @@ const char* pkv_status_string(int32_t st) {
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
     case PKV_ERR_STATE: return "PKV_ERR_STATE";
+    case PKV_ERR_POOL: return "PKV_ERR_POOL";
     default: return "PKV_ERR_UNKNOWN";
   }
 }

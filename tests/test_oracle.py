@@ -327,3 +327,43 @@ def test_planted_wrong_grouping_and_scale_are_caught():
     interleaved = [(h % G) * Hkv + h // G for h in range(G * Hkv)]
     assert _dense_mismatch(q_perm=interleaved) > 1e-3
     assert _dense_mismatch(scale=1.0) > 1e-3
+
+
+# --------------------------------------------------------------- KV append
+
+
+@pytest.mark.parametrize("lens", [[0, 1, 15, 16, 17, 31, 32, 100]])
+@pytest.mark.parametrize("dtype", [W.BF16, W.F16])
+def test_append_stores_the_next_token_where_decode_reads_it(lens, dtype):
+    """Build the cache of N_b + 1 tokens independently, erase token N_b, let
+    the oracle append it back: the pools must match bit for bit, and decode
+    over N_b + 1 tokens must equal torch SDPA on the dense sequences."""
+    rng = np.random.default_rng([11, dtype == W.BF16])
+    B, Hq, Hkv, d = len(lens), 8, 2, 16
+    full = [n + 1 for n in lens]
+    q, kd, vd = random_dense(rng, B, Hq, Hkv, d, full, dtype)
+    kp, vp, bt = scatter_dense(kd, vd, full, perm_seed=5)
+    before_k, before_v = kp.copy(), vp.copy()
+    k_new = np.stack([kd[b][:, n, :] for b, n in enumerate(lens)])  # [B, Hkv, d]
+    v_new = np.stack([vd[b][:, n, :] for b, n in enumerate(lens)])
+    nan = np.uint16(0x7FC0)
+    for b, n in enumerate(lens):  # erase token N_b
+        before_k[bt[b, n // 16], :, n % 16, :] = nan
+        before_v[bt[b, n // 16], :, n % 16, :] = nan
+    k2, v2 = O.append_tokens(before_k, before_v, bt, np.array(lens), k_new, v_new)
+    np.testing.assert_array_equal(k2, kp)
+    np.testing.assert_array_equal(v2, vp)
+    assert (before_k[bt[0, 0], :, 0, :] == nan).all()  # inputs untouched
+    got = O.decode(q, k2, v2, bt, np.array(full), dtype)
+    np.testing.assert_allclose(got, sdpa_reference(q, kd, vd, full, dtype), rtol=1e-12,
+                               atol=1e-14)
+
+
+def test_append_skips_rows_whose_page_is_outside_the_pool():
+    k = np.zeros((4, 1, 16, 8), np.uint16)
+    v = np.zeros_like(k)
+    bt = np.array([[2], [9], [-1]], np.int32)
+    kn = np.full((3, 1, 8), 7, np.uint16)
+    k2, v2 = O.append_tokens(k, v, bt, np.array([5, 5, 5]), kn, kn)
+    assert (k2[2, 0, 5] == 7).all() and (v2[2, 0, 5] == 7).all()
+    assert int((k2 != 0).sum()) == 8  # rows 1 and 2 wrote nothing
