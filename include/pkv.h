@@ -177,7 +177,10 @@ typedef struct pkv_plan_stats {
  * (-inf, 0, 0). m need not be the range's exact maximum: any reference at
  * or above it by a bounded amount represents the same state. */
 typedef struct pkv_workspace_layout {
-  int64_t items_offset;  /* int32x4 {b*Hkv+g, page_begin, page_end, slot} */
+  int64_t items_offset;  /* int32x8 {b*Hkv+g, page_begin, page_end, slot,
+                            row_base, row_count, 0, 0}: row_base / row_count
+                            are the first slot and the range count of
+                            (b, g); a zero-fill item has slot -1 */
   int64_t meta_offset;   /* int32x2 per sequence (WORKQUEUE, BUCKETED);
                             BUCKETED: then int32 per sequence, the rows of
                             the buckets one bucket after another */
@@ -235,8 +238,9 @@ pkv_status pkv_plan_layout_get(const pkv_plan* plan,
                                pkv_workspace_layout* layout);
 
 /* Copy the host image of what pkv_plan_upload sends (upload_bytes of
- * pkv_plan_stats): the work-queue items (int32x4
- * {b*Hkv+g, page_begin, page_end, slot} at items_offset), the per-sequence
+ * pkv_plan_stats): the work-queue items (int32x8
+ * {b*Hkv+g, page_begin, page_end, slot, row_base, row_count, 0, 0} at
+ * items_offset), the per-sequence
  * (slot_base, S_b) pairs at meta_offset and the zeroed merge counters at
  * counters_offset, laid out exactly as in the workspace. `bytes` must be at
  * least upload_bytes (0 is fine when the plan uploads nothing). */

@@ -211,9 +211,11 @@ def pkv_plan_layout_get(plan: int) -> dict:
     return _struct_dict(s)
 
 
-def pkv_plan_queue_get(plan: int, batch: int, num_kv_heads: int | None = None):
-    """Host image of the upload: (items int32 [n, 4], meta int32 [B, 2],
-    counters int32 [B*Hkv] or empty)."""
+def pkv_plan_queue_get(plan: int, batch: int, num_kv_heads: int | None = None,
+                       full: bool = False):
+    """Host image of the upload: (items int32 [n, 4] = {b*Hkv+g, page_begin,
+    page_end, slot} (all 8 fields with ``full``), meta int32 [B, 2], counters
+    int32 [B*Hkv] or empty)."""
     lay = pkv_plan_layout_get(plan)
     need = pkv_plan_stats_get(plan)["upload_bytes"]
     buf = np.zeros(max(need, 1), dtype=np.uint8)
@@ -223,12 +225,13 @@ def pkv_plan_queue_get(plan: int, batch: int, num_kv_heads: int | None = None):
     def cut(off, nbytes):
         return img[off:off + nbytes] if off + nbytes <= need else img[:0]
 
-    items = cut(lay["items_offset"], 16 * lay["num_items"])
+    items = cut(lay["items_offset"], 32 * lay["num_items"])
     has_meta = lay["counters_offset"] > lay["meta_offset"]  # sections are packed
     meta = cut(lay["meta_offset"], 8 * batch) if has_meta else img[:0]
     cnt = (cut(lay["counters_offset"], 4 * batch * num_kv_heads)
            if num_kv_heads is not None else img[:0])
-    return (items.view(np.int32).reshape(-1, 4).copy(),
+    it = items.view(np.int32).reshape(-1, 8)
+    return ((it if full else it[:, :4]).copy(),
             meta.view(np.int32).reshape(-1, 2).copy(),
             cnt.view(np.int32).copy())
 

@@ -35,6 +35,9 @@ HIP_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Preload the leading kernel arguments into SGPRs at wave launch (the
+    # partial kernel passes its prologue's arguments first for this).
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -438,14 +438,6 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ ws_m,
   }
 }
 
-// Slots of (sequence b, KV head g): (first slot, count). Split grid: S cells
-// per row in cell order. Work queue: sequence b's table entry (first slot of
-// the sequence, S_b), KV head g's S_b slots following one another.
-__device__ __forceinline__ SeqMeta row_slots(const PartialParams& a, int b, int g, SeqMeta wq) {
-  if (a.mode == PKV_MODE_WORKQUEUE) return {wq.slot_base + g * wq.splits, wq.splits};
-  return {(b * a.num_kv_heads + g) * a.num_splits, a.num_splits};
-}
-
 // --------------------------------------------------- fused merge (tail)
 //
 // Called by every workgroup of (sequence b, KV head g) after it has written
@@ -504,7 +496,26 @@ __device__ void finish_group(const PartialParams& a, int b, int g, SeqMeta row) 
 //    Softmax weights move from the MFMA layout to this one through a tiny
 //    per-wave LDS buffer. acc[G][8] per lane.
 template <int DT, int G, int D>
-__global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
+// The arguments the prologue needs first come as leading scalars, so that
+// the hardware can preload them into SGPRs at wave launch (gfx950 kernel
+// argument preloading) instead of the first instructions waiting for a
+// load from the argument segment; the rest stay in `rest`, loaded when used.
+__global__ __launch_bounds__(kThreads) void partial_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const Item* __restrict__ items, int32_t mode,
+    int32_t num_splits, int32_t split_chunk, int32_t num_kv_heads, int32_t stride,
+    int32_t num_q_heads, PartialParams rest) {
+  PartialParams a = rest;
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.items = items;
+  a.mode = mode;
+  a.num_splits = num_splits;
+  a.split_chunk = split_chunk;
+  a.num_kv_heads = num_kv_heads;
+  a.stride = stride;
+  a.num_q_heads = num_q_heads;
   constexpr int W = kWavesPerGroup;
   constexpr int P = kPageTokens;
   constexpr int NKI = D / 32;     // K: 1 KiB DMA runs per page = MFMA steps
@@ -541,6 +552,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
   // ---- which range this workgroup owns ----
   int b, g, pb, pe, slot = 0;
   bool early = false;  // range known before the row length
+  SeqMeta row;         // (first slot, range count) of (b, g), for the merge
   if (a.mode == PKV_MODE_WORKQUEUE) {
     const Item it = a.items[blockIdx.x];
     b = it.bg / Hkv;
@@ -548,6 +560,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     pb = it.page_begin;
     pe = it.page_end;
     slot = it.slot;
+    row = {it.row_base, it.row_count};
     early = true;
   } else if (a.mode == PKV_MODE_SPLIT) {
     const int S = a.num_splits;
@@ -567,25 +580,14 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
       pe = min(pb + chunk, pages);
     }
     slot = cell;
+    row = {bg * S, S};
   } else {
     b = blockIdx.x / Hkv;
     g = blockIdx.x - b * Hkv;
     pb = 0;
     pe = 0x7fffffff;
+    row = {0, 0};  // unsplit: no merge
   }
-  // The row's partial-state slots, for the merge in the tail (the work
-  // queue's per-row table is loaded here, off the tail's critical path).
-  // It is a vector load (an atomic one: the compiler would otherwise pick a
-  // scalar load, and the next wait on any scalar load would wait for it),
-  // left undefined in the other modes so no register copy waits for it here.
-  SeqMeta qrow_meta;
-  if (a.mode == PKV_MODE_WORKQUEUE) {
-    const uint64_t v = __hip_atomic_load(
-        reinterpret_cast<uint64_t*>(const_cast<SeqMeta*>(a.meta + b)), __ATOMIC_RELAXED,
-        __HIP_MEMORY_SCOPE_WORKGROUP);
-    qrow_meta = {(int32_t)(uint32_t)v, (int32_t)(uint32_t)(v >> 32)};
-  }
-
   const int t16 = lane & 15;   // token of this lane in the MFMA result
   const int hq = lane >> 4;    // head quad of this lane in the MFMA result
   const int vr = lane / VL;
@@ -642,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
       }
     }
     if (a.mode != PKV_MODE_UNSPLIT && a.fused && slot >= 0)
-      finish_group<DT, G, D>(a, b, g, row_slots(a, b, g, qrow_meta));
+      finish_group<DT, G, D>(a, b, g, row);
     return;
   }
 
@@ -882,7 +884,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams a) {
     }
   }
   if (a.mode != PKV_MODE_UNSPLIT && a.fused)
-    finish_group<DT, G, D>(a, b, g, row_slots(a, b, g, qrow_meta));
+    finish_group<DT, G, D>(a, b, g, row);
 }
 
 // ------------------------------------------------------------ merge kernel
@@ -915,7 +917,9 @@ using MergeLaunch = void (*)(dim3, hipStream_t, const MergeParams&);
 
 template <int DT, int G, int D>
 void launch_partial(dim3 grid, hipStream_t s, const PartialParams& p) {
-  hipLaunchKernelGGL((partial_kernel<DT, G, D>), grid, dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((partial_kernel<DT, G, D>), grid, dim3(kThreads), 0, s, p.q,
+                     p.block_table, p.seq_lens, p.items, p.mode, p.num_splits, p.split_chunk,
+                     p.num_kv_heads, p.stride, p.num_q_heads, p);
 }
 
 template <int DT, int G, int D>

@@ -22,13 +22,20 @@ constexpr int kPageTokens = 16;
 #endif
 constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 
-// Work-queue item as the partial kernel reads it (16 bytes).
+// Work-queue item as the partial kernel reads it (32 bytes, one scalar
+// load). It also names its row's slots (first slot of (b, g) and the row's
+// range count), so the merge in the partial kernel's tail needs no other
+// table.
 struct Item {
   int32_t bg;          // b * Hkv + g
   int32_t page_begin;  // first page of the range (logical page index)
   int32_t page_end;    // one past the last page
-  int32_t slot;        // partial-state slot this range writes
+  int32_t slot;        // partial-state slot this range writes (-1: zero-fill item)
+  int32_t row_base;    // first slot of (b, g)
+  int32_t row_count;   // ranges of (b, g)
+  int32_t pad0, pad1;
 };
+static_assert(sizeof(Item) == 32, "item layout");
 
 struct SeqMeta {
   int32_t slot_base;  // first slot of sequence b

@@ -258,7 +258,8 @@ pkv_status build(pkv_plan& p) {
           for (int32_t g = 0; g < Hkv; ++g)
             for (int32_t si = 0; si < Sb; ++si)
               p.items.push_back({b * Hkv + g, si * c, std::min(pg, (si + 1) * c),
-                                 (int32_t)(num_slots + (int64_t)g * Sb + si)});
+                                 (int32_t)(num_slots + (int64_t)g * Sb + si),
+                                 (int32_t)(num_slots + (int64_t)g * Sb), Sb, 0, 0});
           num_slots += (int64_t)Hkv * Sb;
           if (num_slots > INT32_MAX / 2) {
             set_error("bucket plan too large");
@@ -269,7 +270,7 @@ pkv_status build(pkv_plan& p) {
         cmax = std::max(cmax, c);
       } else if (p.fused) {
         for (int32_t b : rows)
-          for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1});
+          for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1, 0, 0, 0, 0});
         fills += (int32_t)rows.size() * Hkv;
       }
       for (int32_t b : rows) p.rows.push_back(b);
@@ -292,12 +293,13 @@ pkv_status build(pkv_plan& p) {
       for (int32_t g = 0; g < Hkv; ++g)
         for (int32_t si = 0; si < Sb; ++si)
           p.items.push_back({b * Hkv + g, si * chunk, std::min(pg, (si + 1) * chunk),
-                             (int32_t)(num_slots + (int64_t)g * Sb + si)});
+                             (int32_t)(num_slots + (int64_t)g * Sb + si),
+                             (int32_t)(num_slots + (int64_t)g * Sb), Sb, 0, 0});
       // An empty row has no range; with the merge fused into the partial
       // kernel nothing else would write its (zero) output, so it gets one
       // zero-fill item per KV head (slot -1, no pages).
       if (Sb == 0 && p.fused)
-        for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1});
+        for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1, 0, 0, 0, 0});
       num_slots += (int64_t)Hkv * Sb;
       smax = std::max(smax, Sb);
       if (num_slots > INT32_MAX / 2) {

@@ -338,3 +338,22 @@ def test_zero_batch_plan():
     st = P.pkv_plan_stats_get(h)
     assert st["grid"] == 0 and st["kv_tokens"] == 0
     P.pkv_plan_destroy(h)
+
+
+@pytest.mark.parametrize("mode", ["workqueue", "bucketed"])
+@pytest.mark.parametrize("lens", RAGGED)
+def test_items_name_their_row_slots(mode, lens):
+    """Each item carries (first slot, range count) of its (b, g) row, equal
+    to what the per-row table says; zero-fill items carry (0, 0)."""
+    Hkv = 8
+    h = plan(lens, mode)
+    items, meta, _ = P.pkv_plan_queue_get(h, len(lens), Hkv, full=True)
+    for bg, p0, p1, slot, base, count, z0, z1 in items:
+        b, g = bg // Hkv, bg % Hkv
+        assert z0 == z1 == 0
+        if slot < 0:
+            assert (p0, p1, base, count) == (0, 0, 0, 0)
+            continue
+        assert base == meta[b][0] + g * meta[b][1] and count == meta[b][1]
+        assert 0 <= slot - base < count
+    P.pkv_plan_destroy(h)
