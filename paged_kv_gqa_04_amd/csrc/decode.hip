@@ -214,6 +214,17 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(u32x4 a, u32x4 b, floatx4 c) {
 }
 
 
+// Workgroup barrier over the LDS data written with ds_write (the staged
+// table): waits for this wave's LDS instructions, not for its K/V loads in
+// flight. A __syncthreads() would drain those too (the direct-to-LDS loads
+// count as LDS writes for a fence), and so would an LDS-only fence. The ring
+// slots those loads fill are each wave's own and are read only after an
+// explicit vmcnt wait. The memory clobber keeps the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Read one ring slot back from LDS: wait until at most VM vector-memory
 // loads are outstanding (the slot's own direct-to-LDS loads have landed),
 // then read this lane's K pieces (at the per-lane LDS byte addresses ka[])
@@ -330,11 +341,11 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ ws_m,
                                           uint16_t* __restrict__ out_row) {
   constexpr int NC = G * D / 4;          // float4 columns of one state
   constexpr int NSUB = kThreads / NC;    // slot subsets accumulated side by side
-  constexpr int PER = kMergeBatch;
-  constexpr int SB = PER * NSUB;         // slots per acc batch
   constexpr int SPW = 64 / G;            // slots per lane round
   constexpr int K = 4;                   // lane rounds per weight round
   constexpr int TPH = K * SPW;           // slots per weight round
+  constexpr int PER = kMergeBatch < TPH / NSUB ? kMergeBatch : TPH / NSUB;
+  constexpr int SB = PER * NSUB;         // slots per acc batch
   constexpr int W = kWavesPerGroup;
   constexpr int LOG2G = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
   static_assert(NSUB >= 1 && NSUB * NC == kThreads, "layout");
@@ -691,11 +702,14 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   // re-reads one 16-byte word of the chunk's first page instead, so the
   // number of loads in flight behind any slot is fixed and the wait before
   // computing a slot is a constant vmcnt.
-  auto issue_page = [&](int sl, int k) {
+  // With `given`, `phys_in` is the page's table entry, already in hand (the
+  // first pages of a chunk); otherwise the entry is read from the staged
+  // table.
+  auto issue_page = [&](int sl, int k, bool given = false, int phys_in = 0) {
     const bool real = k < cnt;  // wave-uniform
     const int ks = real ? k : 0;
     const int lp = cb + wave + W * ks;
-    int phys = __builtin_amdgcn_readfirstlane(s_bt[wave + W * ks]);
+    int phys = given ? phys_in : __builtin_amdgcn_readfirstlane(s_bt[wave + W * ks]);
     const bool ok = (uint64_t)(uint32_t)phys < (uint64_t)a.num_pages;
     ntok_ring[sl] = ok ? min(P, n - lp * P) : 0;
     phys = ok ? phys : 0;
@@ -810,20 +824,35 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     const int span = min(pe - cb, kBtChunk);
     if (cb != pb) __syncthreads();  // every wave is done with the last chunk
     if (cb != pb || !early) stage_table(cb, span);
-    __syncthreads();
     cnt = span > wave ? (span - wave + W - 1) / W : 0;
-    if (cnt == 0) continue;
+    // The first NB pages of this wave take their table entries straight from
+    // memory (scalar loads, in flight with the staging), so the first K/V
+    // loads go out before the barrier that publishes the staged table; the
+    // wave then waits at that barrier with them in flight. Every wave passes
+    // exactly one such barrier per chunk (a wave with no pages here too).
+    if (cnt == 0) {
+      lds_barrier();
+      continue;
+    }
+    int e[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) e[i] = bt_row[cb + min(wave + W * i, span - 1)];
     // Nothing else is in flight here (q and the table have landed); saying
     // so keeps the compiler from guarding the q registers inside the ring.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i) issue_page(i, i);
+    for (int i = 0; i < NB - 1; ++i) issue_page(i, i, true, i < cnt ? e[i] : e[0]);
     for (int k = 0; k < cnt; k += NB) {
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
         const int kk = k + r;
         if (kk >= cnt) break;
-        issue_page((r + NB - 1) % NB, kk + NB - 1);
+        if (kk == 0) {
+          issue_page(NB - 1, NB - 1, true, NB - 1 < cnt ? e[NB - 1] : e[0]);
+          lds_barrier();  // the staged table is complete (K/V loads stay in flight)
+        } else {
+          issue_page((r + NB - 1) % NB, kk + NB - 1);
+        }
         compute_page(fetch_page(r));
       }
     }
