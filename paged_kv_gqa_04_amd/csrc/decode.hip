@@ -636,7 +636,16 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     }
   };
   const int n = a.seq_lens[b];
-  if (early) stage_table(pb, min(min(pe, a.stride) - pb, kBtChunk));
+  // With the range known early, the first pages' entries of this wave (see
+  // the page loop) are loaded now too, in flight with the staging.
+  int e_first[kRingSlots];
+  if (early) {
+    const int span0 = min(min(pe, a.stride) - pb, kBtChunk);
+#pragma unroll
+    for (int i = 0; i < kRingSlots; ++i)
+      e_first[i] = span0 > 0 ? bt_row[pb + min(wave + kWavesPerGroup * i, span0 - 1)] : 0;
+    stage_table(pb, span0);
+  }
   // Never past the device's own length, nor past the block-table row.
   pe = min(pe, min((n + P - 1) / P, a.stride));
 
@@ -836,7 +845,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     }
     int e[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) e[i] = bt_row[cb + min(wave + W * i, span - 1)];
+    for (int i = 0; i < NB; ++i)
+      e[i] = (cb == pb && early) ? e_first[i] : bt_row[cb + min(wave + W * i, span - 1)];
     // Nothing else is in flight here (q and the table have landed); saying
     // so keeps the compiler from guarding the q registers inside the ring.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
