@@ -208,6 +208,52 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
     }
 
 
+def time_graph(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, merge="fused"):
+    """The same steps launched from a HIP graph: one graph holds one decode
+    per pool copy (so the copies still rotate) and is replayed back to back;
+    returns µs per step."""
+    import torch
+    B = len(dev["seq_lens_host"])
+    shape = P.make_shape(B, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                         dev["block_table_host"].shape[1], dev["num_pages"], spec.dtype,
+                         dev["sm_scale"])
+    plan = P.Plan(shape, dev["seq_lens_host"], P.make_opts(mode, splits, chunk, merge=merge))
+    plan.upload()
+    out = torch.empty_like(dev["q"])
+    pools = dev["replicas"][:replicas]
+
+    def one(r):
+        plan.decode(dev["q"], pools[r][0], pools[r][1], dev["block_table"], dev["seq_lens"], out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for r in range(len(pools)):
+            one(r)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(len(pools)):
+            one(r)
+    reps = max(1, steps // len(pools))
+    for _ in range(max(1, warmup // len(pools))):
+        graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e = ev.create(2)
+    ev.record(e[0], stream)
+    for _ in range(reps):
+        graph.replay()
+    ev.record(e[1], stream)
+    torch.cuda.synchronize()
+    us = ev.ms(e[0], e[1]) / (reps * len(pools)) * 1e3
+    ev.destroy(e)
+    del graph
+    plan.close()
+    return us
+
+
 def sweep(P, dev, spec, replicas, ev, a):
     """Policy calibration: time unsplit, split over a range of S and the work
     queue over a range of chunk sizes, plus the policy's own choice."""
@@ -330,6 +376,8 @@ def main():
     ap.add_argument("--identity-table", action="store_true",
                     help="paging diagnostic: the same cache with each sequence's pages "
                          "consecutive in the pool (identity block table)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph")
     ap.add_argument("--append", action="store_true",
                     help="also time the append step (new-token K/V written through "
                          "the block table) on the workload")
@@ -452,6 +500,11 @@ def main():
             "us_per_step": round(ra["step_us"], 2),
             "gbps": round(sa["algorithmic_bytes"] / (ra["step_us"] * 1e-6) / 1e9, 1),
         }
+    if a.graph:
+        gus = time_graph(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev,
+                         a.merge)
+        line["graph"] = {"us_per_step": round(gus, 2),
+                         "gbps": round(alg / (gus * 1e-6) / 1e9, 1)}
     if a.append:
         line["append"] = time_append(P, dev, spec, a.steps, a.warmup, ev)
     if not a.no_cpu and case is not None:
