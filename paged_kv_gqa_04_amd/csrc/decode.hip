@@ -259,13 +259,15 @@ template <int LPP, int VM, typename KArr, typename VArr>
 __device__ __forceinline__ void read_slot(const uint32_t* ka, uint32_t va, KArr& k, VArr& v) {
   u32x4* kk = &k[0];
   if constexpr (LPP == 8) {
-    if constexpr (VM == 8) PKV_READ8("8");
+    if constexpr (VM == 0) PKV_READ8("0");
+    else if constexpr (VM == 8) PKV_READ8("8");
     else if constexpr (VM == 16) PKV_READ8("16");
     else if constexpr (VM == 24) PKV_READ8("24");
     else static_assert(VM == 8, "ring depth");
   } else {
     static_assert(LPP == 4, "loads per page");
-    if constexpr (VM == 4) PKV_READ4("4");
+    if constexpr (VM == 0) PKV_READ4("0");
+    else if constexpr (VM == 4) PKV_READ4("4");
     else if constexpr (VM == 8) PKV_READ4("8");
     else if constexpr (VM == 12) PKV_READ4("12");
     else static_assert(VM == 4, "ring depth");
@@ -706,48 +708,52 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     return base + wave * SLOT_WORDS;
   };
 
-  // Issue one page's LPP direct-to-LDS loads into ring slot `sl`. Always
-  // exactly LPP instructions: step k past the wave's last page (k >= cnt)
-  // re-reads one 16-byte word of the chunk's first page instead, so the
-  // number of loads in flight behind any slot is fixed and the wait before
-  // computing a slot is a constant vmcnt.
-  // With `given`, `phys_in` is the page's table entry, already in hand (the
-  // first pages of a chunk); otherwise the entry is read from the staged
-  // table.
+  // Issue page k of this wave's share of the chunk (k < cnt): its LPP
+  // direct-to-LDS loads into ring slot `sl`. With `given`, `phys_in` is the
+  // page's table entry, already in hand (the first pages of a chunk);
+  // otherwise the entry is read from the staged table. Only real pages are
+  // ever issued, so the loads in flight behind the page being computed are
+  // those of its min(NB - 1, cnt - 1 - k) younger pages, always LPP each.
   auto issue_page = [&](int sl, int k, bool given = false, int phys_in = 0) {
-    const bool real = k < cnt;  // wave-uniform
-    const int ks = real ? k : 0;
-    const int lp = cb + wave + W * ks;
-    int phys = given ? phys_in : __builtin_amdgcn_readfirstlane(s_bt[wave + W * ks]);
+    const int lp = cb + wave + W * k;
+    int phys = given ? phys_in : __builtin_amdgcn_readfirstlane(s_bt[wave + W * k]);
     const bool ok = (uint64_t)(uint32_t)phys < (uint64_t)a.num_pages;
     ntok_ring[sl] = ok ? min(P, n - lp * P) : 0;
     phys = ok ? phys : 0;
     const int64_t tile = ((int64_t)phys * Hkv + g) * TILE;
     const uint16_t* kp = a.k_pool + tile;
     const uint16_t* vp = a.v_pool + tile;
-    const int on = real ? 1 : 0;  // lane offsets vanish for the filler loads
     uint32_t* dst = slot_base(sl);
 #pragma unroll
     for (int kk = 0; kk < NKI; ++kk)
-      __builtin_amdgcn_global_load_lds(GPTR(kp + on * kdma[kk]), LPTR(dst + kk * 256), 16, 0,
+      __builtin_amdgcn_global_load_lds(GPTR(kp + kdma[kk]), LPTR(dst + kk * 256), 16, 0,
                                        kLoadNontemporal);
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
-      __builtin_amdgcn_global_load_lds(GPTR(vp + on * (i * 512 + lane * 8)),
+      __builtin_amdgcn_global_load_lds(GPTR(vp + i * 512 + lane * 8),
                                        LPTR(dst + (NKI + i) * 256), 16, 0, kLoadNontemporal);
   };
 
-  // Wait until slot `sl` has landed (the NB-1 younger pages may stay in
-  // flight), then read this lane's operands back. The wait and the LDS
-  // reads are one asm block: left to itself the compiler cannot tell the
+  // Wait until slot `sl` has landed, with the loads of `younger` later pages
+  // left in flight, then read this lane's operands back. The wait and the
+  // LDS reads are one asm block: left to itself the compiler cannot tell the
   // ring slots apart at the loop back-edge and drains every load in flight.
-  auto fetch_page = [&](int sl) -> Page {
+  auto fetch_page = [&](int sl, int younger) -> Page {
     Page r;
     const uint32_t base = (uint32_t)(uintptr_t)LPTR(slot_base(sl));
     uint32_t ka[NKI];
 #pragma unroll
     for (int i = 0; i < NKI; ++i) ka[i] = base + kofs[i];
-    read_slot<LPP, (NB - 1) * LPP>(ka, base + NKI * 1024 + lane * 16, r.kb, r.v);
+    const uint32_t va = base + NKI * 1024 + lane * 16;
+    if (younger == NB - 1) {
+      read_slot<LPP, (NB - 1) * LPP>(ka, va, r.kb, r.v);
+    } else if (NB > 2 && younger == 1) {
+      read_slot<LPP, LPP>(ka, va, r.kb, r.v);
+    } else if (NB > 3 && younger == 2) {
+      read_slot<LPP, 2 * LPP>(ka, va, r.kb, r.v);
+    } else {
+      read_slot<LPP, 0>(ka, va, r.kb, r.v);
+    }
     r.ntok = ntok_ring[sl];
     return r;
   };
@@ -851,22 +857,23 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     // so keeps the compiler from guarding the q registers inside the ring.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i) issue_page(i, i, true, i < cnt ? e[i] : e[0]);
+    for (int i = 0; i < NB - 1; ++i)
+      if (i < cnt) issue_page(i, i, true, e[i]);
     for (int k = 0; k < cnt; k += NB) {
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
         const int kk = k + r;
         if (kk >= cnt) break;
+        const bool more = kk + NB - 1 < cnt;  // wave-uniform
         if (kk == 0) {
-          issue_page(NB - 1, NB - 1, true, NB - 1 < cnt ? e[NB - 1] : e[0]);
+          if (more) issue_page(NB - 1, NB - 1, true, e[NB - 1]);
           lds_barrier();  // the staged table is complete (K/V loads stay in flight)
-        } else {
+        } else if (more) {
           issue_page((r + NB - 1) % NB, kk + NB - 1);
         }
-        compute_page(fetch_page(r));
+        compute_page(fetch_page(r, more ? NB - 1 : cnt - 1 - kk));
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // drain the filler loads
   }
 
   // ---- combine the wave states, then the workgroup's waves ----
