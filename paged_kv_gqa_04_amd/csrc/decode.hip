@@ -480,7 +480,7 @@ __device__ void finish_group(const PartialParams& a, int b, int g, SeqMeta row) 
     if (last) __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
-  __syncthreads();
+  lds_barrier();  // s_last is published (no memory access of this workgroup is pending)
   if (!s_last) return;
   merge_row<DT, G, D>(a.ws_m, a.ws_l, a.ws_acc, base, count,
                       a.out + ((int64_t)b * a.num_q_heads + g * G) * D);
@@ -651,25 +651,17 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   // Never past the device's own length, nor past the block-table row.
   pe = min(pe, min((n + P - 1) / P, a.stride));
 
+  float* s_acc = reinterpret_cast<float*>(s_ring0);  // [W][G * D], once the ring is done
   if (pb >= pe) {
-    // Empty range: neutral state (or zeros for an empty row), read nothing.
-    for (int e = threadIdx.x; e < G * D; e += kThreads) {
-      const int h = e / D, dd = e - h * D;
-      if (a.mode == PKV_MODE_UNSPLIT || slot < 0) {  // empty row: zeros
-        a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] = 0;
-      } else {
-        st_agent(a.ws_acc + ((int64_t)slot * G + h) * D + dd, 0.0f);
-        if (dd == 0) {
-          st_agent(a.ws_m + (int64_t)slot * G + h, -INFINITY);
-          st_agent(a.ws_l + (int64_t)slot * G + h, 0.0f);
-        }
-      }
+    // Empty range: read nothing; with neutral wave states the tail below
+    // stores a neutral state (or zeros for a row with no tokens). One tail
+    // for both cases keeps the kernel's code, and its cold end, small.
+    for (int e = threadIdx.x; e < W * G * D; e += kThreads) s_acc[e] = 0.0f;
+    if (threadIdx.x < W * G) {
+      s_m[threadIdx.x / G][threadIdx.x % G] = kNoMax;
+      s_l[threadIdx.x / G][threadIdx.x % G] = 0.0f;
     }
-    if (a.mode != PKV_MODE_UNSPLIT && a.fused && slot >= 0)
-      finish_group<DT, G, D>(a, b, g, row);
-    return;
-  }
-
+  } else {
   // This lane's K operand bytes inside a slot (rotated chunks), and the
   // global element offset its K DMA lanes fetch.
   uint32_t kofs[NKI];
@@ -885,8 +877,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = sum_lanes_from<LOG2_VL>(acc[h][e]);
-  float* s_acc = reinterpret_cast<float*>(s_ring0);  // [W][G * D], ring is done
-  __syncthreads();
+  __syncthreads();  // the ring is done: it becomes the combine buffer
   // Each row's first lane writes its own heads. (A readlane from another
   // lane inside a lane-0-only branch is not safe: the compiler may sink the
   // last step of the row sum into the branch, leaving the other lane's
@@ -905,6 +896,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) s_acc[wave * G * D + h * D + lane * 8 + e] = acc[h][e];
   }
+  }  // non-empty range
   __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
     const int h = e / D, dd = e - h * D;
@@ -918,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       L = fmaf(sc, s_l[w][h], L);
       A = fmaf(sc, s_acc[w * G * D + e], A);
     }
-    if (a.mode == PKV_MODE_UNSPLIT) {
+    if (a.mode == PKV_MODE_UNSPLIT || slot < 0) {  // slot < 0: a row with no tokens
       a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] =
           pack1<DT>(L > 0.0f ? A / L : 0.0f);
     } else {
@@ -929,7 +921,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       }
     }
   }
-  if (a.mode != PKV_MODE_UNSPLIT && a.fused)
+  if (a.mode != PKV_MODE_UNSPLIT && a.fused && slot >= 0)
     finish_group<DT, G, D>(a, b, g, row);
 }
 
