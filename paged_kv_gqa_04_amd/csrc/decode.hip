@@ -325,7 +325,7 @@ struct MergeParams {
 // workgroup:
 //  * acc: thread t owns float4 column t % NC of the G x D state and the
 //    slots t / NC, t / NC + NSUB, ...; its first batch of loads is issued
-//    first, so that it shares one memory latency with the m / l loads.
+//    right behind the m / l loads, so that all share one memory latency.
 //  * m / l: every wave reads all of them itself (lane = slot * G + head,
 //    K lane rounds), reduces each head with fixed DPP / permlane trees and
 //    writes its weights to its own LDS area: no cross-wave barrier.
@@ -371,9 +371,8 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ ws_m,
     for (int j = 0; j < PER; ++j)
       av[j] = ld_agent16(racc, (uint32_t)((s0 + sub + j * NSUB) * (G * D) + c * 4) * 4u);
   };
-  load_acc(0);
 
-  float mk[K];
+  float mk[K], lk[K];
   auto load_m = [&](int r0) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -381,16 +380,26 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ ws_m,
       mk[k] = s < count ? ld_agent(ws_m + (int64_t)(base + s) * G + hm) : -INFINITY;
     }
   };
-
-  // Pass 1: running (max, rescaled sum) per lane, then per head.
-  float Mt = -INFINITY, Lt = 0.0f;
-  for (int r0 = 0; r0 < count; r0 += TPH) {
-    float lk[K];
-    load_m(r0);
+  auto load_l = [&](int r0) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int s = r0 + k * SPW + sl;
       lk[k] = s < count ? ld_agent(ws_l + (int64_t)(base + s) * G + hm) : 0.0f;
+    }
+  };
+  // The first round's m / l go out first and the first acc batch right
+  // after: loads return in order, so pass 1 runs while the acc batch is
+  // still arriving.
+  load_m(0);
+  load_l(0);
+  load_acc(0);
+
+  // Pass 1: running (max, rescaled sum) per lane, then per head.
+  float Mt = -INFINITY, Lt = 0.0f;
+  for (int r0 = 0; r0 < count; r0 += TPH) {
+    if (r0 > 0) {
+      load_m(r0);
+      load_l(r0);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
