@@ -555,8 +555,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   constexpr int SLOT_WORDS = LPP * 256;  // one slot: LPP x 64 lanes x 16 B
 
   // K/V ring: each wave owns NB slots. One LDS array per slot (not one
-  // array indexed by slot) lets the compiler tell slots apart. The first
-  // array doubles as the cross-wave combine buffer at the end.
+  // array indexed by slot) lets the compiler tell slots apart. At the end a
+  // wave's slot in the first array holds its state for the cross-wave
+  // combine.
   static_assert(NB >= 2 && NB <= 4, "two to four slot arrays");
   __shared__ __attribute__((aligned(16))) uint32_t s_ring0[W * SLOT_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t s_ring1[W * SLOT_WORDS];
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   __shared__ __attribute__((aligned(16))) float s_p[W][P * G];
   __shared__ float s_m[W][G];
   __shared__ float s_l[W][G];
-  static_assert(G * D <= SLOT_WORDS, "combine buffer fits in one ring array");
+  static_assert(G * D <= SLOT_WORDS, "a wave's combine state fits in one ring slot");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -660,12 +661,16 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   // Never past the device's own length, nor past the block-table row.
   pe = min(pe, min((n + P - 1) / P, a.stride));
 
-  float* s_acc = reinterpret_cast<float*>(s_ring0);  // [W][G * D], once the ring is done
+  // Wave w's combined acc goes to the start of its own first ring slot once
+  // its page loop is over (its own loads and reads are done by then: no
+  // barrier needed before the write).
+  float* s_acc = reinterpret_cast<float*>(s_ring0);  // wave w at w * SLOT_WORDS
   if (pb >= pe) {
     // Empty range: read nothing; with neutral wave states the tail below
     // stores a neutral state (or zeros for a row with no tokens). One tail
     // for both cases keeps the kernel's code, and its cold end, small.
-    for (int e = threadIdx.x; e < W * G * D; e += kThreads) s_acc[e] = 0.0f;
+    for (int e = threadIdx.x; e < W * G * D; e += kThreads)
+      s_acc[(e / (G * D)) * SLOT_WORDS + e % (G * D)] = 0.0f;
     if (threadIdx.x < W * G) {
       s_m[threadIdx.x / G][threadIdx.x % G] = kNoMax;
       s_l[threadIdx.x / G][threadIdx.x % G] = 0.0f;
@@ -886,7 +891,6 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = sum_lanes_from<LOG2_VL>(acc[h][e]);
-  __syncthreads();  // the ring is done: it becomes the combine buffer
   // Each row's first lane writes its own heads. (A readlane from another
   // lane inside a lane-0-only branch is not safe: the compiler may sink the
   // last step of the row sum into the branch, leaving the other lane's
@@ -903,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave * G * D + h * D + lane * 8 + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) s_acc[wave * SLOT_WORDS + h * D + lane * 8 + e] = acc[h][e];
   }
   }  // non-empty range
   __syncthreads();
@@ -917,7 +921,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     for (int w = 0; w < W; ++w) {
       const float sc = fast_exp2(s_m[w][h] - M);
       L = fmaf(sc, s_l[w][h], L);
-      A = fmaf(sc, s_acc[w * G * D + e], A);
+      A = fmaf(sc, s_acc[w * SLOT_WORDS + e], A);
     }
     if (a.mode == PKV_MODE_UNSPLIT || slot < 0) {  // slot < 0: a row with no tokens
       a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] =
