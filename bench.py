@@ -359,8 +359,10 @@ def cpu_baseline(case, target_s=10.0, cap_s=30.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # The GPU needs ~10 ms of this load to reach its steady clocks: after 20
+    # warm-up steps the long step measures ~3% slower than after 500.
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", default="long")
     ap.add_argument("--mode", default=None)
     ap.add_argument("--splits", type=int, default=None)
