@@ -633,30 +633,34 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   // away (entries inside the table row only), overlapping the length load.
   __shared__ int32_t s_bt[kBtChunk];
   const int32_t* bt_row = a.block_table + (int64_t)b * a.stride;
-  auto stage_table = [&](int c0, int span) {  // all loads first, then the LDS writes
-    constexpr int U = kBtChunk / kThreads;
-    int v[U];
+  constexpr int U = kBtChunk / kThreads;
+  int st_v[U];  // this thread's entries of the chunk being staged
+  auto stage_load = [&](int c0, int span) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = threadIdx.x + u * kThreads;
-      v[u] = i < span ? bt_row[c0 + i] : 0;
+      st_v[u] = i < span ? bt_row[c0 + i] : 0;
     }
+  };
+  auto stage_store = [&](int span) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = threadIdx.x + u * kThreads;
-      if (i < span) s_bt[i] = v[u];
+      if (i < span) s_bt[i] = st_v[u];
     }
   };
   const int n = a.seq_lens[b];
   // With the range known early, the first pages' entries of this wave (see
-  // the page loop) are loaded now too, in flight with the staging.
+  // the page loop) are loaded now too, in flight with the staging loads;
+  // the staged entries are written to LDS only after the first K/V loads
+  // have gone out.
   int e_first[kRingSlots];
   if (early) {
     const int span0 = min(min(pe, a.stride) - pb, kBtChunk);
 #pragma unroll
     for (int i = 0; i < kRingSlots; ++i)
       e_first[i] = span0 > 0 ? bt_row[pb + min(wave + kWavesPerGroup * i, span0 - 1)] : 0;
-    stage_table(pb, span0);
+    stage_load(pb, span0);
   }
   // Never past the device's own length, nor past the block-table row.
   pe = min(pe, min((n + P - 1) / P, a.stride));
@@ -843,8 +847,12 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   // [cb, cb + kBtChunk) go to wave w in the order cb + w, cb + w + W, ...
   for (; cb < pe; cb += kBtChunk) {
     const int span = min(pe - cb, kBtChunk);
+    const bool first_early = cb == pb && early;  // staging loads already in flight
     if (cb != pb) __syncthreads();  // every wave is done with the last chunk
-    if (cb != pb || !early) stage_table(cb, span);
+    if (!first_early) {
+      stage_load(cb, span);
+      stage_store(span);
+    }
     cnt = span > wave ? (span - wave + W - 1) / W : 0;
     // The first NB pages of this wave take their table entries straight from
     // memory (scalar loads, in flight with the staging), so the first K/V
@@ -852,19 +860,25 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     // wave then waits at that barrier with them in flight. Every wave passes
     // exactly one such barrier per chunk (a wave with no pages here too).
     if (cnt == 0) {
+      if (first_early) stage_store(span);
       lds_barrier();
       continue;
     }
     int e[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      e[i] = (cb == pb && early) ? e_first[i] : bt_row[cb + min(wave + W * i, span - 1)];
-    // Nothing else is in flight here (q and the table have landed); saying
-    // so keeps the compiler from guarding the q registers inside the ring.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      e[i] = first_early ? e_first[i] : bt_row[cb + min(wave + W * i, span - 1)];
+    // Everything older than the first pages' loads (q, the staging loads)
+    // must have landed by the wait below, on every path: that keeps the
+    // compiler from guarding the q registers inside the ring. The first
+    // chunk of an early range waits after issuing its first pages (NB - 1
+    // of them, or all at once when it has fewer), the others before.
+    if (!first_early || cnt < NB - 1) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
       if (i < cnt) issue_page(i, i, true, e[i]);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NB - 1) * LPP));
+    if (first_early) stage_store(span);  // the staged entries go to LDS now
     for (int k = 0; k < cnt; k += NB) {
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
