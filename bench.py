@@ -336,9 +336,14 @@ def time_append(P, dev, spec, steps, warmup, ev):
             "gbps": round(nbytes / (us * 1e-6) / 1e9, 1), "rows": int(B)}
 
 
-def cpu_baseline(case, target_s=10.0, cap_s=30.0):
-    """Time the CPU oracle on the bench workload until ~target_s of work."""
+def cpu_baseline(case, target_s=10.0, cap_s=30.0, single_thread=False):
+    """Time the CPU oracle on the bench workload until ~target_s of work
+    (with the BLAS pool limited to one thread when `single_thread`)."""
     from oracle import paged_gqa as O
+    if single_thread:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            return cpu_baseline(case, target_s, cap_s)
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -520,6 +525,10 @@ def main():
             "sample": f"whole {spec.name} step (all {B} sequence(s) x {spec.num_kv_heads} "
                       f"KV heads), float64 numpy oracle, median of {reps_done} runs",
         }
+        sec1, reps1, _ = cpu_baseline(case, target_s=5.0, cap_s=15.0, single_thread=True)
+        line["cpu_baseline"]["single_thread"] = {
+            "value": round(alg / sec1 / 1e9, 3), "us_per_step": round(sec1 * 1e6, 1),
+            "cores": 1, "sample": f"the same step, BLAS limited to 1 thread, median of {reps1} runs"}
     print(json.dumps(line), flush=True)
 
 
