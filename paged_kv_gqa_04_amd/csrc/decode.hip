@@ -8,10 +8,13 @@
 // fp32. The state of the range is written as a partial (m, l, acc) for the
 // merge kernel, or, when the range is the whole row, normalised into out.
 //
-// Merge kernel: one wave per (sequence, query head); combines the row's
-// partial states in split-index order: M = max m_s, weights exp(m_s - M),
-// out = sum w_s acc_s / sum w_s l_s (Methodology 1, the separate merge
-// kernel that combines the states exactly).
+// Merge: combines a (sequence, KV head) row's partial states for its G
+// query heads in split-index order: M = max m_s, weights exp(m_s - M),
+// out = sum w_s acc_s / sum w_s l_s (Methodology 1, the merge kernel that
+// combines the states exactly). By default the last workgroup of the row to
+// finish its range runs it at the end of the partial kernel (one launch per
+// step); the separate merge kernel (one workgroup per row) runs the same
+// code.
 //
 // The step is HBM-bound: every K/V byte is read once and each element feeds
 // only G multiply-adds (ai-trend study note, "Why it was needed": decode reads
@@ -34,7 +37,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 #define GPTR(p) ((__attribute__((address_space(1))) void*)(p))
 #define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -62,17 +64,6 @@ constexpr int kWaitVmcnt0 = waitcnt_vm(0);
 constexpr int kLoadNontemporal = 2;
 
 // ---------------------------------------------------------------- helpers
-
-template <int DT>
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  if constexpr (DT == PKV_BF16) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-  } else {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
-                                  __builtin_bit_cast(f16x2_t, b), c, false);
-  }
-}
 
 template <int DT>
 __device__ __forceinline__ void unpack2(uint32_t u, float& lo, float& hi) {
@@ -128,17 +119,6 @@ __device__ __forceinline__ float4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over aligned groups of N consecutive lanes (N = 4 or 8), result in
-// every lane of the group. DPP: quad_perm [1,0,3,2], [2,3,0,1], then
-// row_half_mirror pairs the two quads of each 8-lane half.
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp_mov<0xB1>(v);
-  v += dpp_mov<0x4E>(v);
-  if constexpr (N == 8) v += dpp_mov<0x141>(v);
-  return v;
 }
 
 // Cross-row exchanges (gfx950): with both operands equal, permlane16_swap
