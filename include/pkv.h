@@ -339,6 +339,25 @@ pkv_status pkv_append(const pkv_shape* shape, const void* k_new, const void* v_n
                       void* k_pool, void* v_pool, const int32_t* block_table,
                       const int32_t* seq_lens, int32_t* new_seq_lens, hipStream_t stream);
 
+/* pkv_append and pkv_decode in one launch (ZimaSpace post and ai-trend study
+ * note, "How it works": a step first places the new token's K/V through the
+ * block table, then decode reads the cache through it). Row b's new token
+ * (k_new / v_new as in pkv_append, 16-byte aligned) goes to position
+ * seq_lens[b], and the step attends over seq_lens[b] + 1 tokens, so `plan`
+ * must have been built (and uploaded) for the lengths seq_lens[b] + 1 and
+ * its page must already be in the table (pkv_append_prepare). The token's
+ * page is read by no other row in the step (a page shared with another row
+ * must not receive the token). k_pool / v_pool are written only at the new
+ * tokens' slots; new_seq_lens (or NULL, never aliasing seq_lens) receives
+ * seq_lens[b] + 1. The outputs and the pools after the call equal those of
+ * pkv_append followed by pkv_decode bit for bit. Errors: those of
+ * pkv_decode, and PKV_ERR_INVALID for a null or misaligned k_new / v_new
+ * or an aliased new_seq_lens. */
+pkv_status pkv_decode_append(const pkv_plan* plan, const void* q, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int32_t* new_seq_lens, void* out, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* pkv_status_string(int32_t status);
 

@@ -36,6 +36,7 @@ from ._pkv import (  # noqa: F401
     pkv_append,
     pkv_append_prepare,
     pkv_decode,
+    pkv_decode_append,
     pkv_decode_marked,
     pkv_last_error,
     pkv_plan_create,
@@ -92,6 +93,11 @@ class Plan:
     def decode(self, q, k_pool, v_pool, block_table, seq_lens, out, stream=None) -> None:
         pkv_decode(self.handle, q, k_pool, v_pool, block_table, seq_lens, out,
                    _stream() if stream is None else stream)
+
+    def decode_append(self, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, out,
+                      new_seq_lens=None, stream=None) -> None:
+        pkv_decode_append(self.handle, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens,
+                          out, new_seq_lens, _stream() if stream is None else stream)
 
     def close(self) -> None:
         if self.handle:

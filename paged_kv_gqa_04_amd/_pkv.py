@@ -108,6 +108,7 @@ SIGNATURES = {
                                        C.POINTER(C.c_int32)]),
     "pkv_pool_release_row": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32, C.c_int32]),
     "pkv_append": (C.c_int32, [C.POINTER(pkv_shape), _P, _P, _P, _P, _P, _P, _P, _P]),
+    "pkv_decode_append": (C.c_int32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -239,6 +240,14 @@ def pkv_plan_queue_get(plan: int, batch: int, num_kv_heads: int | None = None,
 def pkv_decode(plan: int, q, k_pool, v_pool, block_table, seq_lens, out, stream=0) -> None:
     _check(LIB.pkv_decode(plan, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                           _ptr(seq_lens), _ptr(out), _ptr(stream) or None), "pkv_decode")
+
+
+def pkv_decode_append(plan: int, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens,
+                      out, new_seq_lens=None, stream=0) -> None:
+    _check(LIB.pkv_decode_append(plan, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                 _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                                 _ptr(new_seq_lens), _ptr(out), _ptr(stream) or None),
+           "pkv_decode_append")
 
 
 def pkv_decode_marked(plan: int, q, k_pool, v_pool, block_table, seq_lens, out, stream=0,

@@ -278,6 +278,11 @@ struct PartialParams {
   int32_t split_chunk;  // SPLIT: range size shared by every row (0: per row, from seq_lens)
   int32_t fused;     // last-arriving workgroup of a row merges its states
   float scale_log2;  // sm_scale * log2(e)
+  // Folded append (null k_new: none): row b's new token ([B, Hkv, d] each)
+  // goes to position seq_lens[b], and the step attends over seq_lens[b] + 1.
+  const uint16_t* __restrict__ k_new;
+  const uint16_t* __restrict__ v_new;
+  int32_t* __restrict__ new_seq_lens;  // seq_lens[b] + 1 (may be null)
 };
 
 struct MergeParams {
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       pe = pb + a.split_chunk;
       early = true;
     } else {
-      const int pages = (a.seq_lens[b] + P - 1) / P;
+      const int pages = (a.seq_lens[b] + (a.k_new ? 1 : 0) + P - 1) / P;
       const int chunk = pages > 0 ? (pages + S - 1) / S : 1;  // row-local
       pb = s * chunk;
       pe = min(pb + chunk, pages);
@@ -629,7 +634,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       if (i < span) s_bt[i] = st_v[u];
     }
   };
-  const int n = a.seq_lens[b];
+  // Row length, with the folded append's new token (at position n - 1).
+  const int n = a.seq_lens[b] + (a.k_new ? 1 : 0);
   // With the range known early, the first pages' entries of this wave (see
   // the page loop) are loaded now too, in flight with the staging loads;
   // the staged entries are written to LDS only after the first K/V loads
@@ -644,6 +650,24 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   }
   // Never past the device's own length, nor past the block-table row.
   pe = min(pe, min((n + P - 1) / P, a.stride));
+
+  // Folded append: the workgroup whose range holds the new token's page
+  // (exactly one per (row, KV head)) swaps the token into its operand
+  // registers when it computes that page, and writes it to the pools at the
+  // end (no other workgroup reads that page in this launch).
+  const int app_page = a.k_new && n > 0 ? (n - 1) / P : -1;
+  const bool app_owner = app_page >= pb && app_page < pe;  // workgroup-uniform
+  const int app_slot = (n - 1) % P;
+  int app_phys = 0;
+  u32x4 k_tok[NKI], v_tok;  // this lane's pieces of the new token, in operand layout
+  if (app_owner) {
+    app_phys = bt_row[app_page];
+    const uint16_t* kn = a.k_new + ((int64_t)b * Hkv + g) * D;
+    const uint16_t* vn = a.v_new + ((int64_t)b * Hkv + g) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKI; ++kk) k_tok[kk] = *(const u32x4*)(kn + 32 * kk + 8 * hq);
+    v_tok = *(const u32x4*)(vn + (lane % VL) * 8);
+  }
 
   // Wave w's combined acc goes to the start of its own first ring slot once
   // its page loop is over (its own loads and reads are done by then: no
@@ -688,11 +712,13 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     u32x4 kb[NKI];
     u32x4 v[NVI];
     int ntok;  // valid tokens of the page (0 if its table entry is bad)
+    int lp;    // page index in the row
   };
 
   int cb = pb;  // first page of the staged chunk
   int cnt = 0;  // pages of the chunk this wave computes
   int ntok_ring[NB];
+  int lp_ring[NB];
   auto slot_base = [&](int sl) -> uint32_t* {
     uint32_t* base = sl == 0 ? s_ring0 : sl == 1 ? s_ring1 : sl == 2 ? s_ring2 : s_ring3;
     return base + wave * SLOT_WORDS;
@@ -709,6 +735,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     int phys = given ? phys_in : __builtin_amdgcn_readfirstlane(s_bt[wave + W * k]);
     const bool ok = (uint64_t)(uint32_t)phys < (uint64_t)a.num_pages;
     ntok_ring[sl] = ok ? min(P, n - lp * P) : 0;
+    lp_ring[sl] = lp;
     phys = ok ? phys : 0;
     const int64_t tile = ((int64_t)phys * Hkv + g) * TILE;
     const uint16_t* kp = a.k_pool + tile;
@@ -745,12 +772,20 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       read_slot<LPP, 0>(ka, va, r.kb, r.v);
     }
     r.ntok = ntok_ring[sl];
+    r.lp = lp_ring[sl];
     return r;
   };
 
   float* sp = s_p[wave];
 
-  auto compute_page = [&](const Page& r) {
+  auto compute_page = [&](Page& r) {
+    if (app_owner && r.lp == app_page) {  // the new token's page: its slot from registers
+#pragma unroll
+      for (int kk = 0; kk < NKI; ++kk) r.kb[kk] = t16 == app_slot ? k_tok[kk] : r.kb[kk];
+#pragma unroll
+      for (int i = 0; i < NVI; ++i)
+        r.v[i] = i * TPI + vr == app_slot ? v_tok : r.v[i];
+    }
     floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < NKI; ++kk) c = mfma_16x16x32<DT>(qa[kk], r.kb[kk], c);
@@ -871,7 +906,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
         } else if (more) {
           issue_page((r + NB - 1) % NB, kk + NB - 1);
         }
-        compute_page(fetch_page(r, more ? NB - 1 : cnt - 1 - kk));
+        Page pg = fetch_page(r, more ? NB - 1 : cnt - 1 - kk);
+        compute_page(pg);
       }
     }
   }
@@ -928,6 +964,20 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       }
     }
   }
+  // Folded append: the owner writes the new token to the pools (for later
+  // steps; a table entry outside the pool writes nothing, as in pkv_append),
+  // and the row's first range of KV head 0 reports the new length.
+  if (app_owner && wave == 0 && (uint64_t)(uint32_t)app_phys < (uint64_t)a.num_pages) {
+    const int64_t row0 = (((int64_t)app_phys * Hkv + g) * P + app_slot) * D;
+    if (t16 == 0) {
+      uint16_t* kp = const_cast<uint16_t*>(a.k_pool) + row0;
+#pragma unroll
+      for (int kk = 0; kk < NKI; ++kk) *(u32x4*)(kp + 32 * kk + 8 * hq) = k_tok[kk];
+    }
+    if (vr == 0) *(u32x4*)(const_cast<uint16_t*>(a.v_pool) + row0 + lane * 8) = v_tok;
+  }
+  if (a.k_new && a.new_seq_lens && g == 0 && pb == 0 && threadIdx.x == 0)
+    a.new_seq_lens[b] = n;
   if (a.mode != PKV_MODE_UNSPLIT && a.fused && slot >= 0)
     finish_group<DT, G, D>(a, b, g, row);
 }
@@ -1011,13 +1061,35 @@ pkv_status hip_fail(const char* what, hipError_t e) {
   return PKV_ERR_HIP;
 }
 
+// One folded append (the new tokens and where the new lengths go), or none.
+struct AppendArgs {
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  int32_t* new_seq_lens = nullptr;
+};
+
 pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, const int32_t* seq_lens, void* out,
-                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1, hipEvent_t ev2) {
+                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1, hipEvent_t ev2,
+                       const AppendArgs& app = AppendArgs{}) {
   clear_error();
   if (!p) {
     set_error("plan is NULL");
     return PKV_ERR_INVALID;
+  }
+  if (app.k_new || app.v_new) {
+    if (!app.k_new || !app.v_new) {
+      set_error("k_new and v_new must both be given");
+      return PKV_ERR_INVALID;
+    }
+    if (!aligned(app.k_new, 16) || !aligned(app.v_new, 16) || !aligned(app.new_seq_lens, 4)) {
+      set_error("k_new/v_new must be 16-byte and new_seq_lens 4-byte aligned");
+      return PKV_ERR_INVALID;
+    }
+    if (app.new_seq_lens && (const void*)app.new_seq_lens == (const void*)seq_lens) {
+      set_error("new_seq_lens must not alias seq_lens (other workgroups still read it)");
+      return PKV_ERR_INVALID;
+    }
   }
   const pkv_shape& s = p->shape;
   if (s.batch == 0) {
@@ -1073,6 +1145,9 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
   pp.num_splits = p->num_splits;
   pp.split_chunk = p->split_chunk;
   pp.scale_log2 = s.sm_scale * kLog2e;
+  pp.k_new = (const uint16_t*)app.k_new;
+  pp.v_new = (const uint16_t*)app.v_new;
+  pp.new_seq_lens = app.new_seq_lens;
 
   MergeParams mp{};
   mp.ws_m = pp.ws_m;
@@ -1220,6 +1295,23 @@ pkv_status pkv_decode(const pkv_plan* p, const void* q, const void* k_pool, cons
                       hipStream_t stream) {
   return pkv::decode_impl(p, q, k_pool, v_pool, block_table, seq_lens, out, stream, nullptr,
                           nullptr, nullptr);
+}
+
+pkv_status pkv_decode_append(const pkv_plan* p, const void* q, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int32_t* new_seq_lens, void* out, hipStream_t stream) {
+  pkv::AppendArgs app;
+  app.k_new = k_new;
+  app.v_new = v_new;
+  app.new_seq_lens = new_seq_lens;
+  if (!k_new || !v_new) {
+    pkv::clear_error();
+    pkv::set_error("k_new and v_new are required");
+    return PKV_ERR_INVALID;
+  }
+  return pkv::decode_impl(p, q, k_pool, v_pool, block_table, seq_lens, out, stream, nullptr,
+                          nullptr, nullptr, app);
 }
 
 pkv_status pkv_decode_marked(const pkv_plan* p, const void* q, const void* k_pool,
