@@ -336,6 +336,56 @@ def time_append(P, dev, spec, steps, warmup, ev):
             "gbps": round(nbytes / (us * 1e-6) / 1e9, 1), "rows": int(B)}
 
 
+def time_step_with_append(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev):
+    """A decode step that also appends each row's new token, timed two ways
+    over `steps` back-to-back steps: pkv_append then pkv_decode (two
+    launches), and pkv_decode_append (one launch). As in time_append, each
+    row rewrites its last token (position N_b - 1), so the plan for the
+    lengths N_b serves every step."""
+    import torch
+    lens = np.asarray(dev["seq_lens_host"])
+    B, Hkv, d = len(lens), spec.num_kv_heads, spec.head_dim
+    shape = P.make_shape(B, spec.num_q_heads, Hkv, d, dev["block_table_host"].shape[1],
+                         dev["num_pages"], spec.dtype, dev["sm_scale"])
+    plan = P.Plan(shape, lens, P.make_opts(mode, splits, chunk))
+    plan.upload()
+    td = dev["k_pool"].dtype
+    g = torch.Generator(device=dev["k_pool"].device).manual_seed(2)
+    k_new = torch.randn((B, Hkv, d), generator=g, device=dev["k_pool"].device).to(td)
+    v_new = torch.randn((B, Hkv, d), generator=g, device=dev["k_pool"].device).to(td)
+    pos = torch.from_numpy(np.maximum(lens - 1, 0).astype(np.int32)).to(k_new.device)
+    new_lens = torch.empty_like(pos)
+    out = torch.empty_like(dev["q"])
+    pools = dev["replicas"][:replicas]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def two(i):
+        kp, vp = pools[i % len(pools)]
+        P.pkv_append(shape, k_new, v_new, kp, vp, dev["block_table"], pos, new_lens, stream)
+        P.pkv_decode(plan.handle, dev["q"], kp, vp, dev["block_table"], new_lens, out, stream)
+
+    def one(i):
+        kp, vp = pools[i % len(pools)]
+        P.pkv_decode_append(plan.handle, dev["q"], k_new, v_new, kp, vp, dev["block_table"],
+                            pos, out, new_lens, stream)
+
+    res = {}
+    for name, fn in (("append_then_decode_us", two), ("decode_append_us", one)):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e = ev.create(2)
+        ev.record(e[0], stream)
+        for i in range(steps):
+            fn(i)
+        ev.record(e[1], stream)
+        torch.cuda.synchronize()
+        res[name] = round(ev.ms(e[0], e[1]) / steps * 1e3, 2)
+        ev.destroy(e)
+    plan.close()
+    return res
+
+
 def cpu_baseline(case, target_s=10.0, cap_s=30.0, single_thread=False):
     """Time the CPU oracle on the bench workload until ~target_s of work
     (with the BLAS pool limited to one thread when `single_thread`)."""
@@ -514,6 +564,8 @@ def main():
                          "gbps": round(alg / (gus * 1e-6) / 1e9, 1)}
     if a.append:
         line["append"] = time_append(P, dev, spec, a.steps, a.warmup, ev)
+        line["append"]["step"] = time_step_with_append(P, dev, spec, mode, splits, a.chunk,
+                                                       a.steps, a.warmup, replicas, ev)
     if not a.no_cpu and case is not None:
         sec, reps_done, threads = cpu_baseline(case)
         line["cpu_baseline"] = {
