@@ -186,16 +186,22 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
     torch.cuda.synchronize()
     part = [ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
     ev.destroy(evs)
-    # synchronized wall time of a step including host planning + upload
-    sync = []
-    for i in range(min(20, steps)):
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        plan.update(dev["seq_lens_host"])
-        plan.upload()
-        P.pkv_decode(plan.handle, *args(i % len(pools)), stream)
-        torch.cuda.synchronize()
-        sync.append(time.perf_counter() - t)
+    # synchronized wall time of a step including host planning + upload: as
+    # the library runs it (the re-planned image is unchanged, so nothing is
+    # copied), and with the copy forced
+    def sync_wall(force):
+        sync = []
+        for i in range(min(100, steps)):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            plan.update(dev["seq_lens_host"])
+            plan.upload(force=force)
+            P.pkv_decode(plan.handle, *args(i % len(pools)), stream)
+            torch.cuda.synchronize()
+            sync.append(time.perf_counter() - t)
+        return sync
+    sync = sync_wall(False)
+    sync_copy = sync_wall(True)
     plan.close()
     return {
         "stats": stats,
@@ -205,6 +211,7 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
                                       float(np.percentile(part, 90)) * 1e3],
         "wall_us_per_step": wall / steps * 1e6,
         "sync_wall_us_with_plan": float(np.median(sync)) * 1e6,
+        "sync_wall_us_with_plan_copy": float(np.median(sync_copy)) * 1e6,
     }
 
 
@@ -278,7 +285,7 @@ def sweep(P, dev, spec, replicas, ev, a):
         }), flush=True)
 
 
-def ablation(P, dev, spec, replicas, ev, a):
+def ablation(P, dev, spec, replicas, ev, a, seed):
     """The scheduling comparators of the PersistentKV explainer (Results,
     scheduling overhead) on one workload: the policy's choice, the unsplit
     path, the rectangular split grid, the compact work queue and
@@ -291,7 +298,7 @@ def ablation(P, dev, spec, replicas, ev, a):
         r = time_mode(P, dev, spec, mode, 0, 0, a.steps, a.warmup, replicas, ev, merge)
         st = r["stats"]
         print(json.dumps({
-            "workload": spec.name, "seed": a.seed, "mode": mode, "merge": merge,
+            "workload": spec.name, "seed": seed, "mode": mode, "merge": merge,
             "resolved": st["mode_name"], "num_splits": st["num_splits"],
             "chunk_pages": st["chunk_pages"], "grid": st["grid"],
             "launches": st["launches"], "bucket_launches": st["bucket_launches"],
@@ -299,6 +306,7 @@ def ablation(P, dev, spec, replicas, ev, a):
             "us_per_step": round(r["step_us"], 2),
             "gbps": round(st["algorithmic_bytes"] / (r["step_us"] * 1e-6) / 1e9, 1),
             "sync_wall_us_with_plan": round(r["sync_wall_us_with_plan"], 2),
+            "sync_wall_us_with_plan_copy": round(r["sync_wall_us_with_plan_copy"], 2),
         }), flush=True)
 
 
@@ -488,7 +496,7 @@ def main():
         sweep(P, dev, spec, replicas, ev, a)
         return
     if a.ablation:
-        ablation(P, dev, spec, replicas, ev, a)
+        ablation(P, dev, spec, replicas, ev, a, seed)
         return
     r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev, a.merge)
     st = r["stats"]
@@ -530,6 +538,7 @@ def main():
         "algorithmic_bytes_per_step": int(alg),
         "wall_us_per_step": round(r["wall_us_per_step"], 2),
         "sync_wall_us_with_plan": round(r["sync_wall_us_with_plan"], 2),
+        "sync_wall_us_with_plan_copy": round(r["sync_wall_us_with_plan_copy"], 2),
         "partial_kernel_marked_us": round(r["partial_marked_us"], 2),
         "partial_kernel_marked_p10_p90_us": [round(x, 2) for x in r["partial_marked_us_p10_p90"]],
         "roofline": {

@@ -215,9 +215,23 @@ pkv_status pkv_plan_create(const pkv_shape* shape, const int32_t* seq_lens_host,
 /* Re-plan in place for the next step (same shape and options, new lengths);
  * reuses the plan's host buffers. Waits for the plan's previous upload copy
  * to leave its pinned staging buffer. The plan must be uploaded again before
- * the next decode. Errors as pkv_plan_create. (Serving re-forms the batch
- * every step: ai-trend study note, "How it works", step four.) */
+ * the next decode, unless pkv_plan_upload_needed reports otherwise: when the
+ * plan was uploaded and the new queue image is byte for byte the one its
+ * last upload copied (typically when no row gained or lost a page: ranges
+ * are whole pages, and the kernels read the exact lengths from the device
+ * seq_lens) and the bound workspace is large enough, the plan stays
+ * uploaded. Errors as pkv_plan_create. (Serving re-forms the batch every
+ * step: ai-trend study note, "How it works", step four.) */
 pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* seq_lens_host);
+
+/* *needed = 1 if the next decode needs pkv_plan_upload first (never
+ * uploaded, or the last pkv_plan_update changed the queue image or outgrew
+ * the workspace), 0 if the workspace bound by the last upload already holds
+ * the plan's image (valid for decodes ordered after that upload's copy, and
+ * while the caller leaves the workspace untouched). Host-only, no HIP call.
+ * For callers that re-plan every step: skipping the copy saves a
+ * host-to-device transfer per step. Errors: PKV_ERR_INVALID for NULL. */
+pkv_status pkv_plan_upload_needed(const pkv_plan* plan, int32_t* needed);
 
 /* Device workspace the plan needs (bytes, 0 for UNSPLIT). */
 size_t pkv_plan_workspace_bytes(const pkv_plan* plan);

@@ -46,6 +46,7 @@ from ._pkv import (  # noqa: F401
     pkv_plan_stats_get,
     pkv_plan_update,
     pkv_plan_upload,
+    pkv_plan_upload_needed,
     pkv_plan_workspace_bytes,
     pkv_pool_alloc,
     pkv_pool_create,
@@ -82,11 +83,18 @@ class Plan:
     def update(self, seq_lens_host) -> None:
         pkv_plan_update(self.handle, seq_lens_host)
 
-    def upload(self, device="cuda", stream=None) -> None:
+    def upload(self, device="cuda", stream=None, force=False) -> None:
+        """Bind the workspace (allocated here, grown when the plan needs
+        more) and copy the queue image into it. Copies nothing when the
+        workspace already holds the plan's current image (re-planned with no
+        change to it: pkv_plan_upload_needed), unless `force`."""
         import torch
         nb = self.workspace_bytes()
-        if nb and (self.workspace is None or self.workspace.numel() < nb):
+        grown = bool(nb) and (self.workspace is None or self.workspace.numel() < nb)
+        if grown:
             self.workspace = torch.empty(nb, dtype=torch.uint8, device=device)
+        elif not force and not pkv_plan_upload_needed(self.handle):
+            return
         ptr = self.workspace if nb else 0
         pkv_plan_upload(self.handle, ptr, nb, _stream() if stream is None else stream)
 

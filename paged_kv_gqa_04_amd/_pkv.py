@@ -87,6 +87,7 @@ SIGNATURES = {
     "pkv_plan_create": (C.c_int32, [C.POINTER(pkv_shape), C.POINTER(C.c_int32),
                                     C.POINTER(pkv_opts), C.POINTER(_P)]),
     "pkv_plan_update": (C.c_int32, [_P, C.POINTER(C.c_int32)]),
+    "pkv_plan_upload_needed": (C.c_int32, [_P, C.POINTER(C.c_int32)]),
     "pkv_plan_workspace_bytes": (C.c_size_t, [_P]),
     "pkv_plan_upload": (C.c_int32, [_P, _P, C.c_size_t, _P]),
     "pkv_plan_stats_get": (C.c_int32, [_P, C.POINTER(pkv_plan_stats)]),
@@ -183,6 +184,12 @@ def pkv_plan_create(shape: pkv_shape, seq_lens_host, opts: pkv_opts | None = Non
 def pkv_plan_update(plan: int, seq_lens_host) -> None:
     arr, ptr = _lens(seq_lens_host)
     _check(LIB.pkv_plan_update(plan, ptr if arr.size else None), "pkv_plan_update")
+
+
+def pkv_plan_upload_needed(plan: int) -> bool:
+    needed = C.c_int32(1)
+    _check(LIB.pkv_plan_upload_needed(plan, C.byref(needed)), "pkv_plan_upload_needed")
+    return bool(needed.value)
 
 
 def pkv_plan_workspace_bytes(plan: int) -> int:

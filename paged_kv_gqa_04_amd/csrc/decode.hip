@@ -1286,6 +1286,7 @@ pkv_status pkv_plan_upload(pkv_plan* p, void* workspace, size_t workspace_bytes,
     if ((e = hipEventRecord((hipEvent_t)p->upload_event, stream)) != hipSuccess)
       return pkv::hip_fail("hipEventRecord", e);
   }
+  p->copied_bytes = p->upload_bytes;
   p->uploaded = true;
   return PKV_OK;
 }

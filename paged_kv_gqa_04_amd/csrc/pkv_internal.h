@@ -85,8 +85,10 @@ struct pkv_plan {
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
   bool uploaded = false;
-  void* pinned = nullptr;  // pinned staging of [items | meta]
+  void* pinned = nullptr;  // pinned staging of [items | meta]: the image last copied
   size_t pinned_bytes = 0;
+  int64_t copied_bytes = 0;         // length of that image (0: none copied yet)
+  std::vector<char> image_scratch;  // a re-planned image, compared with the copied one
   void* upload_event = nullptr;  // hipEvent_t of the last upload copy
   int device = -1;
 };

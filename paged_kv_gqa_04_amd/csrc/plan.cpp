@@ -454,7 +454,33 @@ pkv_status pkv_plan_update(pkv_plan* p, const int32_t* seq_lens_host) {
   if (st != PKV_OK) return st;
   pkv::wait_upload(p);
   p->seq_lens.assign(seq_lens_host, seq_lens_host + p->shape.batch);
-  return pkv::build(*p);
+  const bool was_uploaded = p->uploaded;
+  st = pkv::build(*p);  // leaves the plan not uploaded
+  if (st != PKV_OK || !was_uploaded) return st;
+  // The workspace still holds the previous image. When the new plan's image
+  // is byte for byte the same (the usual case when no row gained or lost a
+  // page: ranges are whole pages and the kernels read the exact lengths
+  // from the device) and the workspace is large enough, the plan stays
+  // uploaded and the next decode needs no copy.
+  const int64_t nb = p->upload_bytes;
+  if (nb != p->copied_bytes || p->layout.total_bytes > (int64_t)p->workspace_bytes) return st;
+  if (nb > 0) {
+    p->image_scratch.resize((size_t)nb);
+    pkv::write_upload_image(*p, p->image_scratch.data());
+    if (std::memcmp(p->image_scratch.data(), p->pinned, (size_t)nb) != 0) return st;
+  }
+  p->uploaded = true;
+  return st;
+}
+
+pkv_status pkv_plan_upload_needed(const pkv_plan* p, int32_t* needed) {
+  pkv::clear_error();
+  if (!p || !needed) {
+    pkv::set_error("plan or needed is NULL");
+    return PKV_ERR_INVALID;
+  }
+  *needed = p->uploaded ? 0 : 1;
+  return PKV_OK;
 }
 
 size_t pkv_plan_workspace_bytes(const pkv_plan* p) {

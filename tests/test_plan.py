@@ -287,6 +287,19 @@ def test_update_replans_in_place():
     P.pkv_plan_destroy(h)
 
 
+def test_a_plan_that_was_never_uploaded_needs_an_upload():
+    shape = P.make_shape(2, 8, 2, 64, 100, 1000, "bf16")
+    h = P.pkv_plan_create(shape, [100, 200], P.make_opts("workqueue", chunk_pages=2, num_cus=CUS))
+    assert P.pkv_plan_upload_needed(h)
+    P.pkv_plan_update(h, [100, 200])  # unchanged, but nothing was ever copied
+    assert P.pkv_plan_upload_needed(h)
+    from paged_kv_gqa_04_amd import _pkv
+    needed = ctypes.c_int32(7)
+    assert _pkv.LIB.pkv_plan_upload_needed(None, ctypes.byref(needed)) == P.PKV_ERR_INVALID
+    assert _pkv.LIB.pkv_plan_upload_needed(ctypes.c_void_p(h), None) == P.PKV_ERR_INVALID
+    P.pkv_plan_destroy(h)
+
+
 # ------------------------------------------------------------- error codes
 
 
