@@ -118,26 +118,33 @@ def to_identity_table(dev):
 
 def partial_kernel_bytes(stats, spec, batch):
     """Algorithmic bytes the partial kernel moves per launch: K/V of the exact
-    tokens, q, used block-table entries, seq_lens (plus out when unsplit)."""
+    tokens, q, used block-table entries, seq_lens, plus out when that launch
+    writes it (unsplit, or the merge fused into its tail: one launch)."""
     d, Hq = spec.head_dim, spec.num_q_heads
     out_bytes = batch * Hq * d * 2
     b = stats["algorithmic_bytes"] - out_bytes
-    return b + (out_bytes if stats["mode_name"] == "unsplit" else 0)
+    return b + (out_bytes if stats["launches"] == 1 else 0)
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "partial_kernel_long_split32_traffic.md")
+# Committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, by the launch they
+# were taken on: (workload, mode, splits, merge) -> file.
+TRAFFIC_PROFILES = {
+    ("long", "split", 32, "fused"): "partial_kernel_long_split32_traffic.md",
+    ("mixed8", "workqueue", 14, "fused"): "partial_kernel_mixed8_workqueue_traffic.md",
+}
 
 
 def measured_traffic(workload, mode, splits, merge):
     """HBM bytes per partial-kernel launch from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary, scaled by the plain-copy factors it
-    records; None when the workload differs from the profiled one or the
-    kernel source has changed since the counters were taken."""
+    records; None when no summary covers this launch or the kernel source
+    has changed since the counters were taken."""
     import hashlib
-    if (workload, mode, splits, merge) != ("long", "split", 32, "fused"):
+    name = TRAFFIC_PROFILES.get((workload, mode, splits, merge))
+    if name is None:
         return None
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(os.path.join(ROOT, "profiles", name)).read()
         src = open(os.path.join(ROOT, "paged_kv_gqa_04_amd", "csrc", "decode.hip"), "rb").read()
     except OSError:
         return None
