@@ -401,6 +401,82 @@ def time_step_with_append(P, dev, spec, mode, splits, chunk, steps, warmup, repl
     return res
 
 
+def serve_loop(P, name, seed, mode, steps, warmup):
+    """A decode loop as a server runs it, every step on the host clock: the
+    page pool gives a page to each row whose new token opens one (the table
+    goes to the device when it changed), the plan is re-made for the new
+    lengths and its queue copied only when it changed, and one launch
+    appends every row's new token and decodes (pkv_decode_append), then the
+    host waits for it. The ai-trend study note ("How it works", steps two
+    and four) describes this loop; the PersistentKV explainer (Evaluation
+    protocol) reports synchronized wall time including planning. One pool
+    copy only (the appends write into it), so the cache may be served from
+    the Infinity Cache: these are per-step latencies, not bandwidth."""
+    import torch
+    import workloads as W
+    spec = W.CONFIGS[name]
+    total = steps + warmup
+    grow = total // W.PAGE_TOKENS + 2  # pages each row may take
+    case = W.make_case(name, seed, poison=False)
+    B = case.batch
+    # the pool's spare pages, plus room for the growth in a wider table
+    extra = B * grow
+    k = np.concatenate([case.k_pool, case.k_pool[:extra]])
+    v = np.concatenate([case.v_pool, case.v_pool[:extra]])
+    num_pages = case.num_pages + extra
+    stride0 = case.block_table.shape[1]
+    bt = np.full((B, stride0 + grow), -1, np.int32)
+    bt[:, :stride0] = case.block_table
+    lens = case.seq_lens.astype(np.int32).copy()
+    pool = P.Pool(num_pages)
+    pool.alloc(num_pages)
+    used = set()
+    for b in range(B):
+        used.update(int(x) for x in bt[b, :W.pages_for(int(lens[b]))])
+    pool.free(np.array(sorted(set(range(num_pages)) - used), np.int32))
+    td = W.torch_dtype(case.dtype)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kp, vp = dev(k.view(np.int16)).view(td), dev(v.view(np.int16)).view(td)
+    bt_d, lens_d = dev(bt), dev(lens)
+    new_d = torch.empty_like(lens_d)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    q = torch.randn((B, spec.num_q_heads, spec.head_dim), generator=g, device="cuda").to(td)
+    kn = torch.randn((B, spec.num_kv_heads, spec.head_dim), generator=g, device="cuda").to(td)
+    vn = torch.randn((B, spec.num_kv_heads, spec.head_dim), generator=g, device="cuda").to(td)
+    out = torch.empty_like(q)
+    shape = P.make_shape(B, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, bt.shape[1],
+                         num_pages, case.dtype, case.sm_scale)
+    plan = P.Plan(shape, lens + 1, P.make_opts(mode, 0, 0))
+    plan.upload()
+    times, copies, table_updates = [], 0, 0
+    for step in range(total):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        if pool.prepare(lens, bt):
+            bt_d.copy_(torch.from_numpy(bt))
+            table_updates += step >= warmup
+        plan.update(lens + 1)
+        if P.pkv_plan_upload_needed(plan.handle):
+            copies += step >= warmup
+        plan.upload()
+        plan.decode_append(q, kn, vn, kp, vp, bt_d, lens_d, out, new_d)
+        torch.cuda.synchronize()
+        if step >= warmup:
+            times.append(time.perf_counter() - t)
+        lens += 1
+        lens_d, new_d = new_d, lens_d
+    st = plan.stats()
+    plan.close()
+    pool.close()
+    assert np.array_equal(lens_d.cpu().numpy(), lens), "device lengths diverged"
+    us = np.asarray(times) * 1e6
+    return {"serve": name, "seed": seed, "mode": st["mode_name"], "steps": steps,
+            "warmup": warmup, "rows": int(B), "final_kv_tokens": int(lens.sum()),
+            "sync_wall_us_p50": round(float(np.median(us)), 2),
+            "sync_wall_us_p90": round(float(np.percentile(us, 90)), 2),
+            "steps_with_queue_copy": int(copies), "steps_with_table_copy": int(table_updates)}
+
+
 def cpu_baseline(case, target_s=10.0, cap_s=30.0, single_thread=False):
     """Time the CPU oracle on the bench workload until ~target_s of work
     (with the BLAS pool limited to one thread when `single_thread`)."""
@@ -456,6 +532,10 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="time the scheduling comparators (unsplit, rectangular split, "
                          "work queue, exact-length bucketing), one JSON line each")
+    ap.add_argument("--serve", action="store_true",
+                    help="time a serving loop (page allocation, re-planning, queue copy "
+                         "when changed, append folded into the decode, synchronisation) "
+                         "on the host clock, per step")
     ap.add_argument("--sweep", action="store_true",
                     help="time a grid of (mode, splits / chunk) candidates for the "
                          "workload, one JSON line each (policy calibration)")
@@ -482,6 +562,12 @@ def main():
 
     seed = W.SEED_HOLDOUT if a.seed is None else a.seed
     torch.cuda.set_device(0)
+    if a.serve:
+        if a.config == "b64":
+            sys.exit("--serve builds its inputs on the host: not for b64")
+        print(json.dumps(serve_loop(P, a.config, seed, a.mode or "auto", a.steps, a.warmup)),
+              flush=True)
+        return
     spec, dev, case = make_inputs(a.config, seed, "cuda")
     if a.identity_table:
         dev = to_identity_table(dev)
