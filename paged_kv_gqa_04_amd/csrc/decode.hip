@@ -109,6 +109,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const float* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes,
                                            kRawBufferWord3);
 }
+// 16 bytes of a partial state at byte offset `off`, device-scope store.
+__device__ __forceinline__ void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  const u32x4 u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                   __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)off, 0, kCpolSc1);
+}
 // 16 bytes of a partial state at byte offset `off`, device-scope load.
 __device__ __forceinline__ float4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc1);
@@ -941,23 +947,34 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   }
   }  // non-empty range
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += kThreads) {
-    const int h = e / D, dd = e - h * D;
+  // Combine the W wave states: each thread takes four consecutive columns of
+  // one head (one float4 of the G x D state, one pass for G x D <= 4 x 256):
+  // M = max of the waves' references, wave w weighted by 2^(m_w - M), summed
+  // in wave order.
+  for (int e4 = threadIdx.x; e4 < G * D / 4; e4 += kThreads) {
+    const int h = (e4 * 4) / D, dd = e4 * 4 - h * D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.0f, A = 0.0f;
+    float L = 0.0f;
+    float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const float sc = fast_exp2(s_m[w][h] - M);
+      const float4 x = *reinterpret_cast<const float4*>(s_acc + w * SLOT_WORDS + e4 * 4);
       L = fmaf(sc, s_l[w][h], L);
-      A = fmaf(sc, s_acc[w * SLOT_WORDS + e], A);
+      A.x = fmaf(sc, x.x, A.x);
+      A.y = fmaf(sc, x.y, A.y);
+      A.z = fmaf(sc, x.z, A.z);
+      A.w = fmaf(sc, x.w, A.w);
     }
     if (a.mode == PKV_MODE_UNSPLIT || slot < 0) {  // slot < 0: a row with no tokens
-      a.out[((int64_t)b * a.num_q_heads + g * G + h) * D + dd] =
-          pack1<DT>(L > 0.0f ? A / L : 0.0f);
+      const bool any = L > 0.0f;
+      const uint32_t lo = pack1<DT>(any ? A.x / L : 0.0f) | ((uint32_t)pack1<DT>(any ? A.y / L : 0.0f) << 16);
+      const uint32_t hi = pack1<DT>(any ? A.z / L : 0.0f) | ((uint32_t)pack1<DT>(any ? A.w / L : 0.0f) << 16);
+      *(uint2*)(a.out + ((int64_t)b * a.num_q_heads + g * G + h) * D + dd) = make_uint2(lo, hi);
     } else {
-      st_agent(a.ws_acc + ((int64_t)slot * G + h) * D + dd, A);
+      st_agent16(raw_rsrc(a.ws_acc + (int64_t)slot * G * D, G * D * 4), (uint32_t)(h * D + dd) * 4u, A);
       if (dd == 0) {
         st_agent(a.ws_m + (int64_t)slot * G + h, L > 0.0f ? M : -INFINITY);
         st_agent(a.ws_l + (int64_t)slot * G + h, L);
