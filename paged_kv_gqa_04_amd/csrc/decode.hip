@@ -919,14 +919,47 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   }
 
   // ---- combine the wave states, then the workgroup's waves ----
-  // l: sum over the 16 tokens of each MFMA row; acc: over the V rows.
-  constexpr int LOG2_VL = VL == 16 ? 4 : 3;
+  // l: sum over the 16 tokens of each MFMA row; acc: over the V rows (lane
+  // bits log2(VL) .. 5). The acc sums pair up values so that every exchange
+  // moves two of them: with x and y in the two operands, permlane16_swap
+  // leaves rows (x0, y0, x2, y2) and (x1, y1, x3, y3), whose sum holds x's
+  // and y's row-pair sums; permlane32_swap on two such registers leaves
+  // rows (x0, x1, y0, y1) and (x2, x3, y2, y3), whose sum holds four full
+  // sums, one per 16-lane row. Value v[4j + r] ends in row r of red[j], and
+  // v is the flattened acc[G][8] taken row-major by destination row, so row
+  // r holds 2G consecutive entries of it. Each sum adds (row 0 + row 1) +
+  // (row 2 + row 3), after the bit-3 DPP step when VL = 8.
 #pragma unroll
   for (int i = 0; i < 4; ++i) lsum[i] = row16_sum(lsum[i]);
+  constexpr int NR = 2 * G;  // sums per 16-lane row
+  float red[NR];
+  {
+    float v[4 * NR];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = sum_lanes_from<LOG2_VL>(acc[h][e]);
+      for (int j = 0; j < NR; ++j) {
+        const int idx = r * NR + j;  // into the flattened acc[G][8]
+        v[4 * j + r] = acc[idx / 8][idx % 8];
+      }
+    if constexpr (VL == 8) {
+#pragma unroll
+      for (int k = 0; k < 4 * NR; ++k) v[k] += dpp_mov<0x128>(v[k]);
+    }
+    float z[2 * NR];
+#pragma unroll
+    for (int i = 0; i < 2 * NR; ++i) {
+      const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * i]),
+                                                      __float_as_uint(v[2 * i + 1]), false, false);
+      z[i] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[2 * j]),
+                                                      __float_as_uint(z[2 * j + 1]), false, false);
+      red[j] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+  }
   // Each row's first lane writes its own heads. (A readlane from another
   // lane inside a lane-0-only branch is not safe: the compiler may sink the
   // last step of the row sum into the branch, leaving the other lane's
@@ -939,11 +972,13 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
         s_l[wave][4 * hq + i] = lsum[i];
       }
   }
-  if (lane < VL) {
+  if (t16 < VL) {  // with VL = 8, lanes 8..15 of a row hold copies
+    const int r = lane >> 4;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wave * SLOT_WORDS + h * D + lane * 8 + e] = acc[h][e];
+    for (int j = 0; j < NR; ++j) {
+      const int idx = r * NR + j;
+      s_acc[wave * SLOT_WORDS + (idx / 8) * D + t16 * 8 + idx % 8] = red[j];
+    }
   }
   }  // non-empty range
   __syncthreads();
