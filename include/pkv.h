@@ -176,6 +176,11 @@ typedef struct pkv_plan_stats {
  * acc = sum exp(x - m) v over the range; a neutral state is
  * (-inf, 0, 0). m need not be the range's exact maximum: any reference at
  * or above it by a bounded amount represents the same state. */
+/* Bytes between two rows' merge counters in the workspace: each counter has
+ * its own cache lines, so that the workgroups of different rows do not queue
+ * behind each other's atomic increments. */
+#define PKV_COUNTER_STRIDE 256
+
 typedef struct pkv_workspace_layout {
   int64_t items_offset;  /* int32x8 {b*Hkv+g, page_begin, page_end, slot,
                             row_base, row_count, 0, 0}: row_base / row_count
@@ -184,8 +189,9 @@ typedef struct pkv_workspace_layout {
   int64_t meta_offset;   /* int32x2 per sequence (WORKQUEUE, BUCKETED);
                             BUCKETED: then int32 per sequence, the rows of
                             the buckets one bucket after another */
-  int64_t counters_offset; /* int32 per (sequence, KV head): arrivals of the
-                              current step (fused merge); 0 between steps */
+  int64_t counters_offset; /* int32 per (sequence, KV head), PKV_COUNTER_STRIDE
+                              bytes apart: arrivals of the current step
+                              (fused merge); 0 between steps */
   int64_t m_offset;      /* fp32 [num_slots][G] */
   int64_t l_offset;      /* fp32 [num_slots][G] */
   int64_t acc_offset;    /* fp32 [num_slots][G][d] */

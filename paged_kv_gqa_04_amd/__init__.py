@@ -9,6 +9,7 @@ for the workspace allocation and the current stream only.
 from __future__ import annotations
 
 from ._pkv import (  # noqa: F401
+    COUNTER_STRIDE,
     DTYPES,
     LIB_PATH,
     MODE_NAMES,

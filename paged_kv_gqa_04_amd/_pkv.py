@@ -81,6 +81,9 @@ class pkv_workspace_layout(C.Structure):
                 ("group", C.c_int32), ("num_splits", C.c_int32)]
 
 
+# Bytes between two rows' merge counters (PKV_COUNTER_STRIDE in pkv.h).
+COUNTER_STRIDE = 256
+
 # Every function pkv.h declares, with its C signature.
 _P = C.c_void_p
 SIGNATURES = {
@@ -236,8 +239,9 @@ def pkv_plan_queue_get(plan: int, batch: int, num_kv_heads: int | None = None,
     items = cut(lay["items_offset"], 32 * lay["num_items"])
     has_meta = lay["counters_offset"] > lay["meta_offset"]  # sections are packed
     meta = cut(lay["meta_offset"], 8 * batch) if has_meta else img[:0]
-    cnt = (cut(lay["counters_offset"], 4 * batch * num_kv_heads)
-           if num_kv_heads is not None else img[:0])
+    rows = batch * num_kv_heads if num_kv_heads is not None else 0
+    cnt = cut(lay["counters_offset"], COUNTER_STRIDE * rows)
+    cnt = cnt.view(np.int32).reshape(-1, COUNTER_STRIDE // 4)[:, 0] if cnt.size else cnt
     it = items.view(np.int32).reshape(-1, 8)
     return ((it if full else it[:, :4]).copy(),
             meta.view(np.int32).reshape(-1, 2).copy(),

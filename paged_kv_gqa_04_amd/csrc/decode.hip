@@ -273,7 +273,7 @@ struct PartialParams {
   float* __restrict__ ws_m;
   float* __restrict__ ws_l;
   float* __restrict__ ws_acc;
-  int32_t* __restrict__ counters;    // one per (sequence, KV head)
+  int32_t* __restrict__ counters;    // one per (sequence, KV head), PKV_COUNTER_STRIDE bytes apart
   const SeqMeta* __restrict__ meta;  // work queue: (slot_base, S_b) per row
   int64_t num_pages;
   int32_t stride;
@@ -474,10 +474,10 @@ __device__ void finish_group(const PartialParams& a, int b, int g, SeqMeta row) 
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's state stores are done
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(a.counters + bg, 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+    int32_t* const cnt = a.counters + (int64_t)bg * (PKV_COUNTER_STRIDE / 4);
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == count - 1;
-    if (last) __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
   lds_barrier();  // s_last is published (no memory access of this workgroup is pending)

@@ -345,7 +345,7 @@ pkv_status build(pkv_plan& p) {
   off = align_up(meta_end, kAlign);
   L.counters_offset = off;
   const bool counters = mode != PKV_MODE_UNSPLIT && p.fused;
-  const int64_t counters_end = off + (counters ? (int64_t)B * Hkv * 4 : 0);
+  const int64_t counters_end = off + (counters ? (int64_t)B * Hkv * PKV_COUNTER_STRIDE : 0);
   off = align_up(counters_end, kAlign);
   L.m_offset = off;
   off = align_up(off + num_slots * G * 4, kAlign);

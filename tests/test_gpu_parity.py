@@ -288,7 +288,9 @@ def test_fused_counters_reset_between_steps(mode):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(out_bits(out), first)
     lay = plan.layout()
-    cnt = plan.workspace[lay["counters_offset"]:lay["counters_offset"] + 4 * c.batch * c.num_kv_heads]
+    rows = c.batch * c.num_kv_heads
+    import paged_kv_gqa_04_amd as P
+    cnt = plan.workspace[lay["counters_offset"]:lay["counters_offset"] + P.COUNTER_STRIDE * rows]
     assert (cnt.cpu().numpy().view(np.int32) == 0).all()
     plan.close()
 

@@ -86,7 +86,7 @@ def test_workqueue_partitions_rows_without_empty_items(lens, chunk):
     lay = P.pkv_plan_layout_get(h)
     assert st["mode_name"] == "workqueue" and st["launches"] == 1  # fused merge
     assert cnt.shape == (len(lens) * Hkv,) and (cnt == 0).all()
-    assert st["upload_bytes"] == lay["counters_offset"] + 4 * len(lens) * Hkv
+    assert st["upload_bytes"] == lay["counters_offset"] + P.COUNTER_STRIDE * len(lens) * Hkv
     ck = st["chunk_pages"]
     assert chunk == 0 or ck == chunk
     assert len(items) == st["grid"] == lay["num_items"]
