@@ -268,7 +268,7 @@ def time_graph(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, m
     return us
 
 
-def sweep(P, dev, spec, replicas, ev, a):
+def sweep(P, dev, spec, replicas, ev, a, seed):
     """Policy calibration: time unsplit, split over a range of S and the work
     queue over a range of chunk sizes, plus the policy's own choice."""
     lens = np.asarray(dev["seq_lens_host"])
@@ -284,7 +284,7 @@ def sweep(P, dev, spec, replicas, ev, a):
         r = time_mode(P, dev, spec, mode, S, c, a.steps, a.warmup, replicas, ev, a.merge)
         st = r["stats"]
         print(json.dumps({
-            "workload": spec.name, "seed": a.seed, "mode": mode,
+            "workload": spec.name, "seed": seed, "mode": mode,
             "resolved": st["mode_name"], "num_splits": st["num_splits"],
             "chunk_pages": st["chunk_pages"], "grid": st["grid"],
             "us_per_step": round(r["step_us"], 2),
@@ -586,7 +586,7 @@ def main():
     ev = HipEvents()
 
     if a.sweep:
-        sweep(P, dev, spec, replicas, ev, a)
+        sweep(P, dev, spec, replicas, ev, a, seed)
         return
     if a.ablation:
         ablation(P, dev, spec, replicas, ev, a, seed)

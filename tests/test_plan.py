@@ -370,3 +370,10 @@ def test_items_name_their_row_slots(mode, lens):
         assert base == meta[b][0] + g * meta[b][1] and count == meta[b][1]
         assert 0 <= slot - base < count
     P.pkv_plan_destroy(h)
+
+
+def test_counter_stride_matches_the_header():
+    import re
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    m = re.search(r"#define PKV_COUNTER_STRIDE (\d+)", text)
+    assert m and int(m.group(1)) == P.COUNTER_STRIDE and P.COUNTER_STRIDE % 128 == 0
