@@ -126,6 +126,14 @@ def partial_kernel_bytes(stats, spec, batch):
     return b + (out_bytes if stats["launches"] == 1 else 0)
 
 
+def kernel_sources() -> bytes:
+    """The partial kernel's source and the headers it includes, in a fixed
+    order: what a committed counter summary was taken on."""
+    paths = [("paged_kv_gqa_04_amd", "csrc", "decode.hip"),
+             ("paged_kv_gqa_04_amd", "csrc", "pkv_internal.h"), ("include", "pkv.h")]
+    return b"".join(open(os.path.join(ROOT, *p), "rb").read() for p in paths)
+
+
 # Committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, by the launch they
 # were taken on: (workload, mode, splits, merge) -> file.
 TRAFFIC_PROFILES = {
@@ -145,7 +153,7 @@ def measured_traffic(workload, mode, splits, merge):
         return None
     try:
         text = open(os.path.join(ROOT, "profiles", name)).read()
-        src = open(os.path.join(ROOT, "paged_kv_gqa_04_amd", "csrc", "decode.hip"), "rb").read()
+        src = kernel_sources()
     except OSError:
         return None
     fields = dict(l.split(": ", 1) for l in text.splitlines()

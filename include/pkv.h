@@ -177,9 +177,9 @@ typedef struct pkv_plan_stats {
  * (-inf, 0, 0). m need not be the range's exact maximum: any reference at
  * or above it by a bounded amount represents the same state. */
 /* Bytes between two rows' merge counters in the workspace: each counter has
- * its own cache lines, so that the workgroups of different rows do not queue
- * behind each other's atomic increments. */
-#define PKV_COUNTER_STRIDE 256
+ * its own 128-byte cache line, so that the workgroups of different rows do
+ * not queue behind each other's atomic increments. */
+#define PKV_COUNTER_STRIDE 128
 
 typedef struct pkv_workspace_layout {
   int64_t items_offset;  /* int32x8 {b*Hkv+g, page_begin, page_end, slot,

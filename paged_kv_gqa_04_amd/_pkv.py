@@ -82,7 +82,7 @@ class pkv_workspace_layout(C.Structure):
 
 
 # Bytes between two rows' merge counters (PKV_COUNTER_STRIDE in pkv.h).
-COUNTER_STRIDE = 256
+COUNTER_STRIDE = 128
 
 # Every function pkv.h declares, with its C signature.
 _P = C.c_void_p
