@@ -429,9 +429,11 @@ def serve_loop(P, name, seed, mode, steps, warmup):
     B = case.batch
     # the pool's spare pages, plus room for the growth in a wider table
     extra = B * grow
-    k = np.concatenate([case.k_pool, case.k_pool[:extra]])
-    v = np.concatenate([case.v_pool, case.v_pool[:extra]])
+    fill = np.arange(extra) % case.num_pages  # contents of the added pages: any data
+    k = np.concatenate([case.k_pool, case.k_pool[fill]])
+    v = np.concatenate([case.v_pool, case.v_pool[fill]])
     num_pages = case.num_pages + extra
+    assert k.shape[0] == num_pages and v.shape[0] == num_pages
     stride0 = case.block_table.shape[1]
     bt = np.full((B, stride0 + grow), -1, np.int32)
     bt[:, :stride0] = case.block_table
