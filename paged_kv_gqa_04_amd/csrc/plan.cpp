@@ -455,7 +455,8 @@ pkv_status pkv_plan_update(pkv_plan* p, const int32_t* seq_lens_host) {
   pkv::wait_upload(p);
   p->seq_lens.assign(seq_lens_host, seq_lens_host + p->shape.batch);
   const bool was_uploaded = p->uploaded;
-  st = pkv::build(*p);  // leaves the plan not uploaded
+  p->uploaded = false;  // also after a failed re-plan: decode refuses until a new upload
+  st = pkv::build(*p);
   if (st != PKV_OK || !was_uploaded) return st;
   // The workspace still holds the previous image. When the new plan's image
   // is byte for byte the same (the usual case when no row gained or lost a
