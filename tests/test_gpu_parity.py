@@ -69,6 +69,16 @@ def test_mixed8(mixed_case, mode, chunk):
     assert_parity(got, want, f"mixed8/{mode}/chunk={chunk}")
 
 
+@pytest.mark.parametrize("seed", [20260622, 7, 12345])
+@pytest.mark.parametrize("name", ["mixed8", "b4"])
+def test_ragged_batches_other_seeds(name, seed):
+    """The ragged workloads at full size on other draws of lengths, page
+    placement and values, in the mode the policy picks."""
+    c = W.make_case(name, seed)
+    got = run_case(c)
+    assert_parity(got, O.decode_case(c), f"{name}/seed={seed}")
+
+
 @pytest.mark.parametrize("mode", ["unsplit", "split", "workqueue", "auto"])
 def test_b4(mode):
     c = W.make_case("b4")
