@@ -79,6 +79,27 @@ def test_ragged_batches_other_seeds(name, seed):
     assert_parity(got, O.decode_case(c), f"{name}/seed={seed}")
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.F16])
+@pytest.mark.parametrize("mode,S,chunk", [("split", 7, 0), ("workqueue", 0, 8), ("unsplit", 0, 0)])
+def test_wide_logit_range_and_rising_maxima(dtype, mode, S, chunk):
+    """Logits with a wide dynamic range whose maximum keeps rising along the
+    sequence: a softmax scale 6x the default, and each key scaled by
+    1 + 3 t / N (token t of N), so the running maximum of every range is
+    raised again and again (each raise rescales the accumulator) and most
+    weights underflow against the last tokens'. Checked against the
+    float64 oracle at the usual bar."""
+    lens = [3000, 700, 1, 160]
+    c = _mini(lens, dtype=dtype, seed=41, poison=False)
+    k = O.bits_to_f64(c.k_pool, dtype)
+    for b, n in enumerate(lens):
+        for t in range(n):
+            k[c.block_table[b, t // 16], :, t % 16, :] *= 1.0 + 3.0 * t / n
+    c.k_pool = W.to_bits(k.astype(np.float32), dtype)
+    c.sm_scale = 6.0 / math.sqrt(c.head_dim)
+    got = run_case(c, mode=mode, num_splits=S, chunk_pages=chunk)
+    assert_parity(got, O.decode_case(c), f"wide range/{dtype}/{mode}")
+
+
 @pytest.mark.parametrize("mode", ["unsplit", "split", "workqueue", "auto"])
 def test_b4(mode):
     c = W.make_case("b4")
