@@ -29,7 +29,8 @@
  *   block_table   int32 [B, block_table_stride]; entry j of row b is the
  *                 physical page holding logical tokens [j*P, (j+1)*P) of
  *                 sequence b (LLM Primer ch. 8, section 8.1). Entries at or
- *                 beyond ceil(N_b / P) are never read.
+ *                 beyond ceil(N_b / P) never affect the result (they may be
+ *                 loaded, never past the row's block_table_stride entries).
  *   seq_lens      int32 [B]; N_b >= 0. Must hold the same values as the host
  *                 array the plan was built from.
  * Tail slots of a sequence's last page (t >= N_b) may hold anything,
