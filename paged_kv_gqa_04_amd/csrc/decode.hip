@@ -1311,8 +1311,11 @@ pkv_status pkv_plan_upload(pkv_plan* p, void* workspace, size_t workspace_bytes,
       return PKV_ERR_WORKSPACE;
     }
   }
-  p->workspace = workspace;
-  p->workspace_bytes = workspace_bytes;
+  // A plan that needs no workspace keeps none bound: a later re-plan that
+  // needs one then asks for a new upload instead of trusting an unchecked
+  // pointer.
+  p->workspace = need > 0 ? workspace : nullptr;
+  p->workspace_bytes = need > 0 ? workspace_bytes : 0;
   hipError_t e;
   if (p->upload_bytes > 0) {
     const size_t nb = (size_t)p->upload_bytes;

@@ -464,7 +464,14 @@ pkv_status pkv_plan_update(pkv_plan* p, const int32_t* seq_lens_host) {
   // from the device) and the workspace is large enough, the plan stays
   // uploaded and the next decode needs no copy.
   const int64_t nb = p->upload_bytes;
-  if (nb != p->copied_bytes || p->layout.total_bytes > (int64_t)p->workspace_bytes) return st;
+  if (nb != p->copied_bytes) return st;
+  // The bound workspace must also serve the new plan: present, aligned and
+  // large enough whenever the plan needs one. (A plan that needed none, such
+  // as an unsplit one, may have been bound to anything or to nothing.)
+  const int64_t need = p->layout.total_bytes;
+  if (need > 0 && (!p->workspace || (uintptr_t)p->workspace % 256 != 0 ||
+                   need > (int64_t)p->workspace_bytes))
+    return st;
   if (nb > 0) {
     p->image_scratch.resize((size_t)nb);
     pkv::write_upload_image(*p, p->image_scratch.data());

@@ -300,6 +300,27 @@ def test_a_plan_that_was_never_uploaded_needs_an_upload():
     P.pkv_plan_destroy(h)
 
 
+def test_replan_that_needs_a_workspace_is_not_left_uploaded():
+    # An unsplit plan needs no workspace, so its upload accepts anything
+    # (here NULL, or a misaligned address) and makes no HIP call. A re-plan
+    # that now needs a workspace (split grid, separate merge kernel: an empty
+    # queue image, so nothing to compare) must ask for a new upload rather
+    # than keep the unchecked binding.
+    shape = P.make_shape(1, 32, 8, 128, 2048, 4096, "bf16")
+    for ws in (0, 0x1001):
+        h = P.pkv_plan_create(shape, [100], P.make_opts("auto", num_cus=CUS, merge="kernel"))
+        st = P.pkv_plan_stats_get(h)
+        assert st["mode"] == P.PKV_MODE_UNSPLIT and st["workspace_bytes"] == 0
+        P.pkv_plan_upload(h, ws, 1 << 30)
+        assert not P.pkv_plan_upload_needed(h)
+        P.pkv_plan_update(h, [32768])
+        st = P.pkv_plan_stats_get(h)
+        assert st["mode"] == P.PKV_MODE_SPLIT and st["workspace_bytes"] > 0
+        assert st["upload_bytes"] == 0  # same (empty) image as before
+        assert P.pkv_plan_upload_needed(h), f"workspace {ws:#x} kept bound"
+        P.pkv_plan_destroy(h)
+
+
 # ------------------------------------------------------------- error codes
 
 
