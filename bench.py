@@ -10,9 +10,19 @@ block-table entries + seq_lens) divided by that time.
 Inputs are made once and stay in HBM. To keep the 256 MB Infinity Cache from
 serving repeated steps, the timed loop rotates over several identical copies
 of the pools (so each copy is evicted by the others before it is read again).
+Before the timed steps the step runs for --ramp-ms of wall time, so the GPU
+is at its steady clocks whatever --warmup is.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
-                       [--mode split] [--splits 32] [--chunk 0] [--no-cpu]
+The default line also carries: the same K/V bytes read by a plain streaming
+kernel (``stream_ceiling``: the one-pass read ceiling in this run), the
+mixed batch of 8 and the batch-4 regime (``configs``: mixed8 in the policy's
+mode; b4 unsplit, split, work queue and the policy's pick), and the CPU
+oracle on the host (``cpu_baseline``, with the 64-sequence step
+extrapolated from a sample of its rows).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--ramp-ms 100]
+                       [--config long] [--mode split] [--splits 32] [--chunk 0]
+                       [--no-cpu] [--no-configs] [--no-stream]
                        [--merge fused|kernel] [--seed N] [--identity-table]
        python bench.py --config mixed8 --sweep | --ablation   (one line per candidate)
 """
@@ -163,10 +173,32 @@ def measured_traffic(workload, mode, splits, merge):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, merge="fused"):
+def ramp(launch, min_ms):
+    """Run ``launch(i)`` in batches, synchronising between them, until
+    ``min_ms`` of wall time has passed: the GPU reaches its steady clocks
+    under this load (a fixed step count would not: a step can be 0.03 µs or
+    1 ms long). Returns (steps, ms)."""
+    import torch
+    if min_ms <= 0:
+        return 0, 0.0
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(32):
+            launch(n)
+            n += 1
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= min_ms:
+            return n, el
+
+
+def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, merge="fused",
+              ramp_ms=0.0, light=False):
     """Time `steps` back-to-back decode steps (one event pair around all of
-    them: per-step markers would add their own overhead), then the same
-    number of steps with markers around the partial kernel alone."""
+    them: per-step markers would add their own overhead) after a clock ramp
+    of `ramp_ms` and `warmup` more steps; unless `light`, then the same
+    number of steps with markers around the partial kernel alone, and the
+    synchronized wall time with host planning."""
     import torch
     B = len(dev["seq_lens_host"])
     shape = P.make_shape(B, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
@@ -179,6 +211,8 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
     pools = dev["replicas"][:replicas]
     stream = torch.cuda.current_stream().cuda_stream
     args = lambda r: (dev["q"], pools[r][0], pools[r][1], dev["block_table"], dev["seq_lens"], out)
+    ramp_steps, ramp_done = ramp(
+        lambda i: P.pkv_decode(plan.handle, *args(i % len(pools)), stream), ramp_ms)
     for i in range(warmup):
         P.pkv_decode(plan.handle, *args(i % len(pools)), stream)
     torch.cuda.synchronize()
@@ -193,6 +227,10 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
     wall = time.perf_counter() - t0
     step_ms = ev.ms(e_all[0], e_all[1]) / steps
     ev.destroy(e_all)
+    if light:
+        plan.close()
+        return {"stats": stats, "step_us": step_ms * 1e3, "wall_us_per_step": wall / steps * 1e6,
+                "ramp_steps": ramp_steps, "ramp_ms": ramp_done}
     # 2) per-step markers around the partial kernel (includes marker cost)
     evs = ev.create(2 * steps)
     for i in range(steps):
@@ -227,6 +265,8 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
         "wall_us_per_step": wall / steps * 1e6,
         "sync_wall_us_with_plan": float(np.median(sync)) * 1e6,
         "sync_wall_us_with_plan_copy": float(np.median(sync_copy)) * 1e6,
+        "ramp_steps": ramp_steps,
+        "ramp_ms": ramp_done,
     }
 
 
@@ -487,6 +527,124 @@ def serve_loop(P, name, seed, mode, steps, warmup):
             "steps_with_queue_copy": int(copies), "steps_with_table_copy": int(table_updates)}
 
 
+def stream_ceiling(P, dev, kv_bytes, steps, ramp_ms, ev, grids=(512, 1024, 2048)):
+    """The same number of K/V bytes as one step, read once by a plain
+    streaming kernel (half from each pool, rotating over the same pool
+    copies as the decode): the HBM ceiling a one-pass read of these bytes
+    reaches in this run. Returns µs per read for each grid and the best."""
+    import torch
+    each = kv_bytes // 2 // 16 * 16
+    pools = dev["replicas"]
+    if any(t.numel() * t.element_size() < each for kv in pools for t in kv):
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device=pools[0][0].device)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for grid in grids:
+        launch = lambda i: P.pkv_stream_read(pools[i % len(pools)][0], pools[i % len(pools)][1],
+                                             each, grid, sink, stream)
+        ramp(launch, ramp_ms)
+        e = ev.create(2)
+        ev.record(e[0], stream)
+        for i in range(steps):
+            launch(i)
+        ev.record(e[1], stream)
+        torch.cuda.synchronize()
+        res[grid] = ev.ms(e[0], e[1]) / steps * 1e3
+        ev.destroy(e)
+    best = min(res, key=res.get)
+    return {"bytes": int(2 * each), "us_by_grid": {str(g): round(u, 2) for g, u in res.items()},
+            "us": round(res[best], 2), "grid": best,
+            "gbps": round(2 * each / (res[best] * 1e-6) / 1e9, 1)}
+
+
+def replicate(dev, name_touched_bytes, replicas=0):
+    """Enough identical pool copies that each is evicted from the 256 MB
+    Infinity Cache before it is read again."""
+    touched = name_touched_bytes
+    n = replicas or (1 if touched > 4 * MALL_BYTES else
+                     min(8, math.ceil(2 * MALL_BYTES / max(1, touched)) + 1))
+    reps = [(dev["k_pool"], dev["v_pool"])]
+    for _ in range(n - 1):
+        reps.append((dev["k_pool"].clone(), dev["v_pool"].clone()))
+    dev["replicas"] = reps
+    return n
+
+
+def config_line(P, name, seed, steps, warmup, ramp_ms, ev, modes):
+    """Time one workload in each of `modes` (lighter than the headline: no
+    per-step markers); returns a dict per mode with the policy's choice."""
+    import torch
+    spec, dev, _ = make_inputs(name, seed, "cuda")
+    touched = int(np.sum(dev["seq_lens_host"])) * spec.num_kv_heads * spec.head_dim * 4
+    nrep = replicate(dev, touched)
+    B = len(dev["seq_lens_host"])
+    out = {"description": spec.description, "pool_replicas": nrep}
+    for mode in modes:
+        r = time_mode(P, dev, spec, mode, 0, 0, steps, warmup, nrep, ev, ramp_ms=ramp_ms,
+                      light=True)
+        st = r["stats"]
+        alg = st["algorithmic_bytes"]
+        gbps = alg / (r["step_us"] * 1e-6) / 1e9
+        part = partial_kernel_bytes(st, spec, B)
+        entry = {
+            "resolved": st["mode_name"], "num_splits": st["num_splits"],
+            "chunk_pages": st["chunk_pages"], "grid": st["grid"], "launches": st["launches"],
+            "us_per_step": round(r["step_us"], 2), "gbps": round(gbps, 1),
+            "pct_of_peak_hbm": round(100 * gbps / PEAK_HBM_GBPS, 1),
+            "algorithmic_bytes_per_step": int(alg),
+            "ramp_ms": round(r["ramp_ms"], 1), "ramp_steps": r["ramp_steps"],
+        }
+        if st["launches"] == 1:  # the launch is the whole step
+            entry["partial_kernel_frac"] = round(part / (r["step_us"] * 1e-6) / 1e9 /
+                                                 PEAK_HBM_GBPS, 4)
+        out[mode] = entry
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_info():
+    """Host CPU facts for the CPU baseline."""
+    info = {"host_cpus": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return info
+
+
+def cpu_b64_extrapolated(seed, rows=4):
+    """The oracle on a seeded sample of the 64-sequence workload's rows (their
+    pages copied from the device case), scaled up by the token fraction:
+    an extrapolated CPU time for the whole step."""
+    import torch
+    import workloads as W
+    from oracle import paged_gqa as O
+    dev = W.make_device_case("b64", seed, device="cuda")
+    lens = np.asarray(dev["seq_lens_host"])
+    pick = np.sort(np.random.default_rng(seed).choice(len(lens), size=rows, replace=False))
+    sub = W.host_subcase_from_device(dev, pick)
+    del dev
+    torch.cuda.empty_cache()
+    t = time.perf_counter()
+    O.decode_case(sub)
+    sec = time.perf_counter() - t
+    frac = float(lens[pick].sum()) / float(lens.sum())
+    return {"us_per_step": round(sec / frac * 1e6, 1), "kind": "oracle, extrapolated",
+            "sample": f"rows {pick.tolist()} of 64 ({100 * frac:.1f}% of the step's tokens), "
+                      f"one run, scaled by the token fraction",
+            "sample_seconds": round(sec, 2)}
+
+
 def cpu_baseline(case, target_s=10.0, cap_s=30.0, single_thread=False):
     """Time the CPU oracle on the bench workload until ~target_s of work
     (with the BLAS pool limited to one thread when `single_thread`)."""
@@ -516,9 +674,16 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    # The GPU needs ~10 ms of this load to reach its steady clocks: after 20
-    # warm-up steps the long step measures ~3% slower than after 500.
+    # Untimed steps after the clock ramp (the ramp, not this count, brings the
+    # GPU to its steady clocks).
     ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--ramp-ms", type=float, default=100.0,
+                    help="before timing, run the step for at least this many ms of wall "
+                         "time (clock ramp; independent of --warmup)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the mixed-batch and batch-4 sub-results of the default line")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the plain streaming-read ceiling")
     ap.add_argument("--config", default="long")
     ap.add_argument("--mode", default=None)
     ap.add_argument("--splits", type=int, default=None)
@@ -587,12 +752,7 @@ def main():
         splits = a.splits or 0
 
     touched = int(np.sum(dev["seq_lens_host"])) * spec.num_kv_heads * spec.head_dim * 4
-    replicas = a.replicas or (1 if touched > 4 * MALL_BYTES else
-                              min(8, math.ceil(2 * MALL_BYTES / max(1, touched)) + 1))
-    reps = [(dev["k_pool"], dev["v_pool"])]
-    for _ in range(replicas - 1):
-        reps.append((dev["k_pool"].clone(), dev["v_pool"].clone()))
-    dev["replicas"] = reps
+    replicas = replicate(dev, touched, a.replicas)
     ev = HipEvents()
 
     if a.sweep:
@@ -601,7 +761,8 @@ def main():
     if a.ablation:
         ablation(P, dev, spec, replicas, ev, a, seed)
         return
-    r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev, a.merge)
+    r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev, a.merge,
+                  ramp_ms=a.ramp_ms)
     st = r["stats"]
     B = len(dev["seq_lens_host"])
     alg = st["algorithmic_bytes"]
@@ -620,6 +781,8 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "ramp_ms": round(r["ramp_ms"], 1),
+        "ramp_steps": r["ramp_steps"],
         "ms_per_step": round(r["step_us"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -660,8 +823,15 @@ def main():
                                          "launches", "bucket_launches", "partial_bytes",
                                          "upload_bytes")},
     }
+    if not a.no_stream:
+        sc = stream_ceiling(P, dev, int(st["kv_tokens"]) * spec.num_kv_heads * spec.head_dim * 4,
+                            a.steps, a.ramp_ms, ev)
+        if sc is not None:
+            sc["decode_over_stream"] = round(r["step_us"] / sc["us"], 3)
+            line["stream_ceiling"] = sc
     if not a.no_auto and mode != "auto":
-        ra = time_mode(P, dev, spec, "auto", 0, 0, a.steps, a.warmup, replicas, ev)
+        ra = time_mode(P, dev, spec, "auto", 0, 0, a.steps, a.warmup, replicas, ev,
+                       ramp_ms=a.ramp_ms, light=True)
         sa = ra["stats"]
         line["auto"] = {
             "mode": sa["mode_name"], "num_splits": sa["num_splits"],
@@ -678,6 +848,19 @@ def main():
         line["append"] = time_append(P, dev, spec, a.steps, a.warmup, ev)
         line["append"]["step"] = time_step_with_append(P, dev, spec, mode, splits, a.chunk,
                                                        a.steps, a.warmup, replicas, ev)
+    if not a.no_configs and spec.name == "long" and not a.identity_table:
+        # The other configurations the 70% goal names (mixed batch) and the
+        # batch-4 regime question (unsplit vs split vs work queue, and the
+        # policy's pick), measured in the same run.
+        cfgs = {"mixed8": config_line(P, "mixed8", seed, a.steps, a.warmup, a.ramp_ms, ev,
+                                      ["auto"]),
+                "b4": config_line(P, "b4", seed, a.steps, a.warmup, a.ramp_ms, ev,
+                                  ["unsplit", "split", "workqueue", "auto"])}
+        b4 = cfgs["b4"]
+        timed = {m: b4[m]["us_per_step"] for m in ("unsplit", "split", "workqueue")}
+        b4["auto_pick"] = b4["auto"]["resolved"]
+        b4["fastest"] = min(timed, key=timed.get)
+        line["configs"] = cfgs
     if not a.no_cpu and case is not None:
         sec, reps_done, threads = cpu_baseline(case)
         line["cpu_baseline"] = {
@@ -685,6 +868,7 @@ def main():
             "unit": "GB/s",
             "us_per_step": round(sec * 1e6, 1),
             "cores": int(threads),
+            **host_info(),
             "kind": "oracle",
             "sample": f"whole {spec.name} step (all {B} sequence(s) x {spec.num_kv_heads} "
                       f"KV heads), float64 numpy oracle, median of {reps_done} runs",
@@ -693,6 +877,8 @@ def main():
         line["cpu_baseline"]["single_thread"] = {
             "value": round(alg / sec1 / 1e9, 3), "us_per_step": round(sec1 * 1e6, 1),
             "cores": 1, "sample": f"the same step, BLAS limited to 1 thread, median of {reps1} runs"}
+        if spec.name == "long":
+            line["cpu_baseline"]["b64"] = cpu_b64_extrapolated(seed)
     print(json.dumps(line), flush=True)
 
 

@@ -379,6 +379,16 @@ pkv_status pkv_decode_append(const pkv_plan* plan, const void* q, const void* k_
                              const int32_t* block_table, const int32_t* seq_lens,
                              int32_t* new_seq_lens, void* out, hipStream_t stream);
 
+/* Measurement aid: one plain streaming read of bytes_each bytes from each of
+ * the device buffers a and b (16-byte aligned, bytes_each a multiple of 16),
+ * grid workgroups of 256 lanes, nontemporal 16-byte loads, asynchronous on
+ * `stream`. Timed on the decode's K/V bytes it gives the HBM ceiling a
+ * single read of that many bytes reaches on the device. `sink` is a device
+ * word (4-byte aligned) the kernel may write. Errors: PKV_ERR_INVALID,
+ * PKV_ERR_HIP. */
+pkv_status pkv_stream_read(const void* a, const void* b, int64_t bytes_each, int32_t grid,
+                           void* sink, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* pkv_status_string(int32_t status);
 

@@ -56,6 +56,7 @@ from ._pkv import (  # noqa: F401
     pkv_pool_free_pages,
     pkv_pool_release_row,
     pkv_status_string,
+    pkv_stream_read,
     pkv_version,
 )
 

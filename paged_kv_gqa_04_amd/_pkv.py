@@ -113,6 +113,7 @@ SIGNATURES = {
     "pkv_pool_release_row": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32, C.c_int32]),
     "pkv_append": (C.c_int32, [C.POINTER(pkv_shape), _P, _P, _P, _P, _P, _P, _P, _P]),
     "pkv_decode_append": (C.c_int32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "pkv_stream_read": (C.c_int32, [_P, _P, C.c_int64, C.c_int32, _P, _P]),
 }
 
 
@@ -351,3 +352,10 @@ def pkv_append(shape: pkv_shape, k_new, v_new, k_pool, v_pool, block_table, seq_
     _check(LIB.pkv_append(C.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                           _ptr(block_table), _ptr(seq_lens), _ptr(new_seq_lens),
                           _ptr(stream) or None), "pkv_append")
+
+
+def pkv_stream_read(a, b, bytes_each: int, grid: int, sink, stream=0) -> None:
+    """Plain streaming read of ``bytes_each`` bytes of each of ``a`` and ``b``
+    (measurement aid: the HBM ceiling of a one-pass read)."""
+    _check(LIB.pkv_stream_read(_ptr(a), _ptr(b), int(bytes_each), int(grid), _ptr(sink),
+                               _ptr(stream) or None), "pkv_stream_read")

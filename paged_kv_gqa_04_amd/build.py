@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 HOST_SOURCES = ["plan.cpp", "pool.cpp"]  # plain C++, built by the host compiler
-HIP_SOURCES = ["decode.hip", "append.hip"]
+HIP_SOURCES = ["decode.hip", "append.hip", "stream.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
               "-I", os.path.join(ROCM, "include")]

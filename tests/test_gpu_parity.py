@@ -129,9 +129,11 @@ def test_trace_families(name, mode):
 
 
 @pytest.mark.slow
-def test_b64_full_size_sampled():
-    """The largest workload at full size, in the work-queue launch the bench
-    times; checked on a seeded sample of 8 sequences x all 64 heads."""
+def test_b64_full_size():
+    """The largest workload at full size (64 sequences, G = 8, about 2.3M
+    tokens), in the work-queue launch the bench times, checked element by
+    element on every row and head: the rows go to the host four at a time
+    (their pages only), so host memory stays bounded."""
     import paged_kv_gqa_04_amd as P
     dev = W.make_device_case("b64")
     spec = dev["spec"]
@@ -145,9 +147,11 @@ def test_b64_full_size_sampled():
         torch.cuda.synchronize()
     got = out.to(torch.float64).cpu().numpy()
     assert np.isfinite(got).all()
-    rows = np.random.default_rng(W.SEED_HOLDOUT).choice(spec.batch, size=8, replace=False)
-    sub = W.host_subcase_from_device(dev, rows)
-    assert_parity(got[rows], O.decode_case(sub), "b64 sample")
+    for r0 in range(0, spec.batch, 4):
+        rows = list(range(r0, min(spec.batch, r0 + 4)))
+        sub = W.host_subcase_from_device(dev, rows)
+        assert_parity(got[rows], O.decode_case(sub), f"b64 rows {rows[0]}..{rows[-1]}")
+        del sub
 
 
 # ----------------------------------------------------------- split counts
