@@ -379,6 +379,27 @@ pkv_status pkv_decode_append(const pkv_plan* plan, const void* q, const void* k_
                              const int32_t* block_table, const int32_t* seq_lens,
                              int32_t* new_seq_lens, void* out, hipStream_t stream);
 
+/* pkv_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, with the plan's workspace in the library's own
+ * device scratch instead of a caller-bound one. Each call copies the plan's
+ * queue image and zeroed merge counters (host memory the plan owns, built
+ * by pkv_plan_create / pkv_plan_update) into the scratch on `stream`, then
+ * launches exactly as pkv_decode. No pkv_plan_upload is needed; the call
+ * makes no device or pinned-host allocation of any kind.
+ * Limit: the plan's pkv_plan_workspace_bytes must be at most
+ * PKV_STATIC_SCRATCH_BYTES (16 MiB: every configuration up to 64 sequences
+ * of 131072 tokens at G = 8); larger plans get PKV_ERR_WORKSPACE. The
+ * scratch is one array per device, held until the process ends and shared
+ * by every call on that device, which keeps the last call's contents:
+ * calls that overlap on one device (other streams, other threads) race,
+ * so order them (one stream does). Errors: those of pkv_decode, and
+ * PKV_ERR_WORKSPACE as above. */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+pkv_status pkv_decode_static(const pkv_plan* plan, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, hipStream_t stream);
+
 /* Measurement aid: one plain streaming read of bytes_each bytes from each of
  * the device buffers a and b (16-byte aligned, bytes_each a multiple of 16),
  * grid workgroups of 256 lanes, nontemporal 16-byte loads, asynchronous on

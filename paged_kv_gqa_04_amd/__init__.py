@@ -31,6 +31,7 @@ from ._pkv import (  # noqa: F401
     PKV_MODE_BUCKETED,
     PKV_MODE_WORKQUEUE,
     PKV_OK,
+    STATIC_SCRATCH_BYTES,
     PkvError,
     make_opts,
     make_shape,
@@ -39,6 +40,7 @@ from ._pkv import (  # noqa: F401
     pkv_decode,
     pkv_decode_append,
     pkv_decode_marked,
+    pkv_decode_static,
     pkv_last_error,
     pkv_plan_create,
     pkv_plan_destroy,

@@ -114,7 +114,11 @@ SIGNATURES = {
     "pkv_append": (C.c_int32, [C.POINTER(pkv_shape), _P, _P, _P, _P, _P, _P, _P, _P]),
     "pkv_decode_append": (C.c_int32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "pkv_stream_read": (C.c_int32, [_P, _P, C.c_int64, C.c_int32, _P, _P]),
+    "pkv_decode_static": (C.c_int32, [_P, _P, _P, _P, _P, _P, _P, _P]),
 }
+
+# PKV_STATIC_SCRATCH_BYTES in pkv.h: the largest workspace pkv_decode_static takes.
+STATIC_SCRATCH_BYTES = 16 << 20
 
 
 def _load():
@@ -252,6 +256,12 @@ def pkv_plan_queue_get(plan: int, batch: int, num_kv_heads: int | None = None,
 def pkv_decode(plan: int, q, k_pool, v_pool, block_table, seq_lens, out, stream=0) -> None:
     _check(LIB.pkv_decode(plan, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                           _ptr(seq_lens), _ptr(out), _ptr(stream) or None), "pkv_decode")
+
+
+def pkv_decode_static(plan: int, q, k_pool, v_pool, block_table, seq_lens, out, stream=0) -> None:
+    _check(LIB.pkv_decode_static(plan, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                 _ptr(seq_lens), _ptr(out), _ptr(stream) or None),
+           "pkv_decode_static")
 
 
 def pkv_decode_append(plan: int, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens,

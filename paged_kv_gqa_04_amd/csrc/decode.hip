@@ -25,6 +25,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "pkv_internal.h"
 
@@ -1120,10 +1121,12 @@ struct AppendArgs {
   int32_t* new_seq_lens = nullptr;
 };
 
+// `ws_static`: the workspace to use instead of the plan's bound one (the
+// library's own scratch, already holding the plan's image), or null.
 pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, const int32_t* seq_lens, void* out,
                        hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1, hipEvent_t ev2,
-                       const AppendArgs& app = AppendArgs{}) {
+                       const AppendArgs& app = AppendArgs{}, void* ws_static = nullptr) {
   clear_error();
   if (!p) {
     set_error("plan is NULL");
@@ -1159,7 +1162,7 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
     set_error("q/out/k_pool/v_pool must be 16-byte and block_table/seq_lens 4-byte aligned");
     return PKV_ERR_INVALID;
   }
-  if (p->mode != PKV_MODE_UNSPLIT && !p->uploaded) {
+  if (p->mode != PKV_MODE_UNSPLIT && !p->uploaded && !ws_static) {
     set_error("plan has not been uploaded (pkv_plan_upload) since it was built");
     return PKV_ERR_STATE;
   }
@@ -1170,7 +1173,7 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
     set_error("no kernel for head_dim %d, G %d", D, G);
     return PKV_ERR_UNSUPPORTED;
   }
-  char* ws = (char*)p->workspace;
+  char* ws = (char*)(ws_static ? ws_static : p->workspace);
   const pkv_workspace_layout& L = p->layout;
 
   PartialParams pp{};
@@ -1284,9 +1287,83 @@ void release_device_resources(pkv_plan* p) {
   }
 }
 
+// ------------------------------------------------ allocation-free entry
+//
+// The library's own device scratch for pkv_decode_static: one copy per
+// device (a __device__ array), holding a plan's workspace (queue image,
+// merge counters, partial states). Host code never passes the array's name
+// to a kernel or copy: hipGetSymbolAddress gives each device's address,
+// looked up once per device with that device current, and only that
+// address is used.
+constexpr size_t kStaticScratchBytes = PKV_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace pkv
+
+static __device__ __align__(256) unsigned char scratch[pkv::kStaticScratchBytes];
+
+namespace pkv {
+
+pkv_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device %d: the static scratch is kept for devices 0 .. %d", dev, kMaxDevices - 1);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (!ptr || (uintptr_t)ptr % 256) {
+      set_error("static scratch address %p is not 256-byte aligned", ptr);
+      return PKV_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 }  // namespace pkv
 
 extern "C" {
+
+pkv_status pkv_decode_static(const pkv_plan* p, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, hipStream_t stream) {
+  pkv::clear_error();
+  if (!p) {
+    pkv::set_error("plan is NULL");
+    return PKV_ERR_INVALID;
+  }
+  const size_t need = (size_t)p->layout.total_bytes;
+  if (need > pkv::kStaticScratchBytes) {
+    pkv::set_error("the plan needs a %zu-byte workspace; the static scratch holds %zu bytes",
+                   need, pkv::kStaticScratchBytes);
+    return PKV_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    pkv_status st = pkv::static_scratch(&ws);
+    if (st != PKV_OK) return st;
+    // The queue image and zeroed merge counters go in first, on the stream,
+    // from host memory the plan owns: the scratch holds whatever the
+    // previous call on this device left.
+    if (p->upload_bytes > 0) {
+      const hipError_t e = hipMemcpyAsync(ws, p->static_image.data(), (size_t)p->upload_bytes,
+                                          hipMemcpyHostToDevice, stream);
+      if (e != hipSuccess) return pkv::hip_fail("hipMemcpyAsync(static scratch)", e);
+    }
+  }
+  // (a plan that needs no workspace, unsplit, needs no upload either)
+  return pkv::decode_impl(p, q, k_pool, v_pool, block_table, seq_lens, out, stream, nullptr,
+                          nullptr, nullptr, pkv::AppendArgs{}, ws);
+}
 
 pkv_status pkv_plan_upload(pkv_plan* p, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {

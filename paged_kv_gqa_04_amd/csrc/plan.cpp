@@ -374,6 +374,11 @@ pkv_status build(pkv_plan& p) {
     p.upload_bytes = meta_end;
   else
     p.upload_bytes = 0;
+  // The same image in host memory the plan owns, for the entry point that
+  // copies it into the library's own device scratch on every call (and
+  // allocates nothing there).
+  p.static_image.resize((size_t)p.upload_bytes);
+  if (p.upload_bytes > 0) write_upload_image(p, p.static_image.data());
   p.uploaded = false;
   return PKV_OK;
 }

@@ -321,6 +321,25 @@ def test_replan_that_needs_a_workspace_is_not_left_uploaded():
         P.pkv_plan_destroy(h)
 
 
+def test_static_entry_point_refuses_plans_beyond_its_scratch():
+    # 64 rows of 131072 tokens, G = 8, 4-page ranges: a workspace far past
+    # the static scratch. The size is checked before anything touches a
+    # device, so this runs on the CPU.
+    lens = [131072] * 64
+    h = plan(lens, "workqueue", chunk=4, Hq=64, Hkv=8)
+    assert P.pkv_plan_workspace_bytes(h) > P.STATIC_SCRATCH_BYTES
+    with pytest.raises(P.PkvError) as e:
+        P.pkv_decode_static(h, 0, 0, 0, 0, 0, 0)
+    assert e.value.status == P.PKV_ERR_WORKSPACE
+    P.pkv_plan_destroy(h)
+
+
+def test_static_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == P.STATIC_SCRATCH_BYTES
+
+
 # ------------------------------------------------------------- error codes
 
 
