@@ -173,20 +173,6 @@ __device__ __forceinline__ float max_lanes_from(float v) {
   return swap32_max(v);
 }
 
-// Sum / max over the 16 lanes of each row (DPP only).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_mov<0xB1>(v);
-  v += dpp_mov<0x4E>(v);
-  v += dpp_mov<0x124>(v);
-  return v + dpp_mov<0x128>(v);
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_mov<0xB1>(v));
-  v = fmaxf(v, dpp_mov<0x4E>(v));
-  v = fmaxf(v, dpp_mov<0x124>(v));
-  return fmaxf(v, dpp_mov<0x128>(v));
-}
-
 // 16x16x32 matrix-core product on 8-element bf16 / fp16 operands held as
 // raw 16-byte vectors, fp32 accumulate.
 template <int DT>
@@ -200,6 +186,20 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(u32x4 a, u32x4 b, floatx4 c) {
   }
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to one register of two storage values (round to nearest
+// even; lo in bits 0-15).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const float2_t f = {lo, hi};
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+  }
+}
 
 // Workgroup barrier over the LDS data written with ds_write (the staged
 // table): waits for this wave's LDS instructions, not for its K/V loads in
@@ -214,37 +214,54 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Read one ring slot back from LDS: wait until at most VM vector-memory
 // loads are outstanding (the slot's own direct-to-LDS loads have landed),
-// then read this lane's K pieces (at the per-lane LDS byte addresses ka[])
-// and V pieces (va, va + 1 KiB, ...), and wait for them.
-#define PKV_READ8(VMS)                                                                      \
-  asm volatile("s_waitcnt vmcnt(" VMS ")\n"                                                \
-               "ds_read_b128 %0, %8\n"                                                     \
-               "ds_read_b128 %1, %9\n"                                                     \
-               "ds_read_b128 %2, %10\n"                                                    \
-               "ds_read_b128 %3, %11\n"                                                    \
-               "ds_read_b128 %4, %12\n"                                                    \
-               "ds_read_b128 %5, %12 offset:1024\n"                                        \
-               "ds_read_b128 %6, %12 offset:2048\n"                                        \
-               "ds_read_b128 %7, %12 offset:3072\n"                                        \
-               "s_waitcnt lgkmcnt(0)"                                                       \
-               : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(kk[2]), "=&v"(kk[3]), "=&v"(v[0]),        \
-                 "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])                                      \
-               : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va)                    \
+// then read this lane's K pieces (16 bytes at each of the per-lane LDS byte
+// addresses ka[]) and the V^T operand of each 16-column tile T with one
+// transposing read from va[T] (ds_read_b64_tr_b16: in each 16-lane group,
+// lane i receives 16-bit element i % 4 of the 8 bytes addressed by group
+// lanes i / 4 + 4 j, j = 0..3; the mapping was read back on the GPU), and
+// wait for them. At most 12 LDS reads are in flight (the counter holds 15).
+#define PKV_READ8(VMS) \
+  asm volatile("s_waitcnt vmcnt(" VMS ")\n" \
+               "ds_read_b128 %0, %[k0]\n" \
+               "ds_read_b128 %1, %[k1]\n" \
+               "ds_read_b128 %2, %[k2]\n" \
+               "ds_read_b128 %3, %[k3]\n" \
+               "ds_read_b64_tr_b16 %4, %[v0]\n" \
+               "ds_read_b64_tr_b16 %5, %[v1]\n" \
+               "ds_read_b64_tr_b16 %6, %[v2]\n" \
+               "ds_read_b64_tr_b16 %7, %[v3]\n" \
+               "ds_read_b64_tr_b16 %8, %[v4]\n" \
+               "ds_read_b64_tr_b16 %9, %[v5]\n" \
+               "ds_read_b64_tr_b16 %10, %[v6]\n" \
+               "ds_read_b64_tr_b16 %11, %[v7]\n" \
+               "s_waitcnt lgkmcnt(0)" \
+               : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(kk[2]), "=&v"(kk[3]), "=&v"(vraw[0]), \
+                 "=&v"(vraw[1]), "=&v"(vraw[2]), "=&v"(vraw[3]), "=&v"(vraw[4]), \
+                 "=&v"(vraw[5]), "=&v"(vraw[6]), "=&v"(vraw[7]) \
+               : [k0] "v"(ka[0]), [k1] "v"(ka[1]), [k2] "v"(ka[2]), [k3] "v"(ka[3]), \
+                 [v0] "v"(va[0]), [v1] "v"(va[1]), [v2] "v"(va[2]), [v3] "v"(va[3]), \
+                 [v4] "v"(va[4]), [v5] "v"(va[5]), [v6] "v"(va[6]), [v7] "v"(va[7]) \
                : "memory")
-#define PKV_READ4(VMS)                                                                      \
-  asm volatile("s_waitcnt vmcnt(" VMS ")\n"                                                \
-               "ds_read_b128 %0, %4\n"                                                     \
-               "ds_read_b128 %1, %5\n"                                                     \
-               "ds_read_b128 %2, %6\n"                                                     \
-               "ds_read_b128 %3, %6 offset:1024\n"                                         \
-               "s_waitcnt lgkmcnt(0)"                                                       \
-               : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(v[0]), "=&v"(v[1])                       \
-               : "v"(ka[0]), "v"(ka[1]), "v"(va)                                            \
+#define PKV_READ4(VMS) \
+  asm volatile("s_waitcnt vmcnt(" VMS ")\n" \
+               "ds_read_b128 %0, %[k0]\n" \
+               "ds_read_b128 %1, %[k1]\n" \
+               "ds_read_b64_tr_b16 %2, %[v0]\n" \
+               "ds_read_b64_tr_b16 %3, %[v1]\n" \
+               "ds_read_b64_tr_b16 %4, %[v2]\n" \
+               "ds_read_b64_tr_b16 %5, %[v3]\n" \
+               "s_waitcnt lgkmcnt(0)" \
+               : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(vraw[0]), "=&v"(vraw[1]), \
+                 "=&v"(vraw[2]), "=&v"(vraw[3]) \
+               : [k0] "v"(ka[0]), [k1] "v"(ka[1]), [v0] "v"(va[0]), [v1] "v"(va[1]), \
+                 [v2] "v"(va[2]), [v3] "v"(va[3]) \
                : "memory")
 
 template <int LPP, int VM, typename KArr, typename VArr>
-__device__ __forceinline__ void read_slot(const uint32_t* ka, uint32_t va, KArr& k, VArr& v) {
+__device__ __forceinline__ void read_slot(const uint32_t* ka, const uint32_t* va, KArr& k, VArr& vt) {
   u32x4* kk = &k[0];
+  constexpr int NT = LPP == 8 ? 8 : 4;
+  uint64_t vraw[NT];
   if constexpr (LPP == 8) {
     if constexpr (VM == 0) PKV_READ8("0");
     else if constexpr (VM == 8) PKV_READ8("8");
@@ -259,7 +276,13 @@ __device__ __forceinline__ void read_slot(const uint32_t* ka, uint32_t va, KArr&
     else if constexpr (VM == 12) PKV_READ4("12");
     else static_assert(VM == 4, "ring depth");
   }
+#pragma unroll
+  for (int T = 0; T < NT; ++T) {
+    vt[T][0] = (uint32_t)vraw[T];
+    vt[T][1] = (uint32_t)(vraw[T] >> 32);
+  }
 }
+
 
 // ------------------------------------------------------------- parameters
 
@@ -496,25 +519,30 @@ __device__ void finish_group(const PartialParams& a, int b, int g, SeqMeta row) 
 //    1 KiB contiguous runs. K rows are stored with their 16-byte chunks
 //    rotated by the token index (chunk c of token t at slot position
 //    (c + t) mod (2D/16)): every lane still fetches whole row runs, and the
-//    MFMA operand reads below touch distinct LDS banks.
-//  * Logits: S^T = Q K^T on the matrix cores, v_mfma_f32_16x16x32 over d in
-//    D/32 steps. A = Q (16 rows: the G heads of the group, zero-padded),
-//    B = K^T (16 columns: the page's tokens). The 16x16 result gives lane l
-//    token l % 16 and heads 4 (l / 16) .. +3.
-//  * Softmax: one reference maximum per head, shared by the 16 lanes of a
-//    row, raised only when a logit exceeds it by kTau (then l and acc are
-//    rescaled). Masked tokens and padding heads get -inf by select.
-//  * P.V on the vector ALUs in fp32: lane (r = l / (D/8), c = l % (D/8))
-//    owns columns c*8 .. c*8+7 of the tokens r, r + 64/(D/8), ...; the V
-//    pieces it needs are exactly the ones its own DMA lane brought in.
-//    Softmax weights move from the MFMA layout to this one through a tiny
-//    per-wave LDS buffer. acc[G][8] per lane.
+//    MFMA operand reads below touch distinct LDS banks; V rows are rotated
+//    by two chunks per 256-byte row step for the same reason.
+//  * Logits: S^T = K Q^T on the matrix cores, v_mfma_f32_16x16x32 over d in
+//    D/32 steps. A = K (16 rows: the page's tokens), B = Q^T (16 columns:
+//    the G heads of the group, padded by repeats). The 16x16 result gives
+//    lane l head l % 16 and tokens 4 (l / 16) .. +3.
+//  * Softmax: one reference maximum per head, shared by the four lanes of
+//    the head, raised only when a logit exceeds it by kTau (then l and acc
+//    are rescaled). Masked tokens and padding heads get -inf by select.
+//  * P.V on the matrix cores: O^T = V^T P^T, one v_mfma_f32_16x16x32 per
+//    16 columns of d. P^T comes out of the logits product already in the
+//    B-operand layout; it enters as two 16-bit parts, the rounded weights
+//    and their rounding residuals, paired with V twice along k, so P keeps
+//    ~2^-18 relative accuracy. V^T arrives with one transposing LDS read per
+//    tile. The accumulators hold full sums over the wave's tokens: lane l
+//    holds head l % 16 at columns 16 T + 4 (l / 16) .. +3.
 template <int DT, int G, int D>
 // The arguments the prologue needs first come as leading scalars, so that
 // the hardware can preload them into SGPRs at wave launch (gfx950 kernel
 // argument preloading) instead of the first instructions waiting for a
 // load from the argument segment; the rest stay in `rest`, loaded when used.
-__global__ __launch_bounds__(kThreads) void partial_kernel(
+// (At most 256 registers per lane, two waves per SIMD: measured faster than
+// the compiler's own choice even with one workgroup per CU.)
+__global__ __launch_bounds__(kThreads, 2) void partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const Item* __restrict__ items, int32_t mode,
     int32_t num_splits, int32_t split_chunk, int32_t num_kv_heads, int32_t stride,
@@ -539,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   constexpr int TPI = 64 / VL;    // tokens per V load instruction
   constexpr int NVI = P / TPI;    // V loads per lane per page
   constexpr int TILE = P * D;     // elements of one (page, KV head) tile
-  constexpr int GR = (G + 3) / 4;  // 16-lane rows of the MFMA result holding real heads
+  constexpr int NT = D / 16;      // 16-column tiles of the P.V product
   static_assert(G <= 16, "one MFMA tile of heads");
 
   constexpr int LPP = NKI + NVI;         // 16-byte load instructions per page
@@ -555,7 +583,6 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t s_ring1[W * SLOT_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t s_ring2[NB > 2 ? W * SLOT_WORDS : 4];
   __shared__ __attribute__((aligned(16))) uint32_t s_ring3[NB > 3 ? W * SLOT_WORDS : 4];
-  __shared__ __attribute__((aligned(16))) float s_p[W][P * G];
   __shared__ float s_m[W][G];
   __shared__ float s_l[W][G];
   static_assert(G * D <= SLOT_WORDS, "a wave's combine state fits in one ring slot");
@@ -607,10 +634,10 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   const int hq = lane >> 4;    // head quad of this lane in the MFMA result
   const int vr = lane / VL;
 
-  // Q as the MFMA A operand: row t16 = head t16 of the group, k = d in steps
-  // of 32: this lane holds d = 32 kk + 8 hq .. +7. Rows past G repeat real
-  // heads (their logits are masked out), so every lane loads unconditionally
-  // and the loads overlap the table and length loads below.
+  // Q^T as the MFMA B operand: column t16 = head t16 of the group, k = d in
+  // steps of 32: this lane holds d = 32 kk + 8 hq .. +7. Columns past G
+  // repeat real heads (their logits are masked out), so every lane loads
+  // unconditionally and the loads overlap the table and length loads below.
   u32x4 qa[NKI];
   {
     const uint16_t* qrow = a.q + ((int64_t)b * a.num_q_heads + g * G + (t16 % G)) * D;
@@ -667,6 +694,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   const int app_slot = (n - 1) % P;
   int app_phys = 0;
   u32x4 k_tok[NKI], v_tok;  // this lane's pieces of the new token, in operand layout
+  uint32_t v_col[NT];       // the new token's V at columns 16 T + t16 (V^T operand)
   if (app_owner) {
     app_phys = bt_row[app_page];
     const uint16_t* kn = a.k_new + ((int64_t)b * Hkv + g) * D;
@@ -674,6 +702,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
 #pragma unroll
     for (int kk = 0; kk < NKI; ++kk) k_tok[kk] = *(const u32x4*)(kn + 32 * kk + 8 * hq);
     v_tok = *(const u32x4*)(vn + (lane % VL) * 8);
+#pragma unroll
+    for (int T = 0; T < NT; ++T) v_col[T] = vn[16 * T + t16];
   }
 
   // Wave w's combined acc goes to the start of its own first ring slot once
@@ -695,6 +725,27 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   // global element offset its K DMA lanes fetch.
   uint32_t kofs[NKI];
   int kdma[NKI];
+  // V in a slot: token-major rows of RB bytes, the 16-byte chunks of token t
+  // rotated by vrot(t) positions, so that the 16 token rows one transposing
+  // read touches (32 bytes each) spread over all banks. DMA lane `lane` of V
+  // load i fills chunk position 64 i + lane.
+  constexpr int TPB = 256 / RB;  // token rows per 256 bytes
+  auto vrot = [&](int t) { return 2 * ((t / TPB) % (NCH / 2)); };
+  int vdma[NVI];
+#pragma unroll
+  for (int i = 0; i < NVI; ++i) {
+    const int pos = 64 * i + lane;
+    const int t = pos / NCH, c = (pos % NCH - vrot(t) + NCH) % NCH;
+    vdma[i] = t * D + c * 8;
+  }
+  // This lane's transposing-read address for tile T: the 8 bytes of token
+  // 4 hq + t16 / 4 at columns 16 T + 4 (t16 % 4) .. +3.
+  uint32_t vofs[NT];
+#pragma unroll
+  for (int T = 0; T < NT; ++T) {
+    const int t = 4 * hq + t16 / 4, c = 2 * T + (t16 % 4) / 2;
+    vofs[T] = NKI * 1024 + t * RB + ((c + vrot(t)) % NCH) * 16 + 8 * (t16 % 2);
+  }
 #pragma unroll
   for (int kk = 0; kk < NKI; ++kk) {
     kofs[kk] = t16 * RB + ((4 * kk + hq + t16) % NCH) * 16;
@@ -703,21 +754,15 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     kdma[kk] = t * D + (((pch - t) % NCH + NCH) % NCH) * 8;  // t may exceed NCH
   }
 
-  float acc[G][8];
-  float lsum[4], mref[4];  // per head 4 hq + i, shared across a row
+  // O^T tiles: acc[T][i] = output of head t16 at column 16 T + 4 hq + i.
+  floatx4 acc[NT];
+  float lsum = 0.0f, mref = kNoMax;  // head t16; lsum over this lane's tokens
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lsum[i] = 0.0f;
-    mref[i] = kNoMax;
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  for (int T = 0; T < NT; ++T) acc[T] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   struct Page {
     u32x4 kb[NKI];
-    u32x4 v[NVI];
+    uint32_t vt[NT][2];
     int ntok;  // valid tokens of the page (0 if its table entry is bad)
     int lp;    // page index in the row
   };
@@ -754,7 +799,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
                                        kLoadNontemporal);
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
-      __builtin_amdgcn_global_load_lds(GPTR(vp + i * 512 + lane * 8),
+      __builtin_amdgcn_global_load_lds(GPTR(vp + vdma[i]),
                                        LPTR(dst + (NKI + i) * 256), 16, 0, kLoadNontemporal);
   };
 
@@ -768,100 +813,91 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     uint32_t ka[NKI];
 #pragma unroll
     for (int i = 0; i < NKI; ++i) ka[i] = base + kofs[i];
-    const uint32_t va = base + NKI * 1024 + lane * 16;
+    uint32_t va[NT];
+#pragma unroll
+    for (int T = 0; T < NT; ++T) va[T] = base + vofs[T];
     if (younger == NB - 1) {
-      read_slot<LPP, (NB - 1) * LPP>(ka, va, r.kb, r.v);
+      read_slot<LPP, (NB - 1) * LPP>(ka, va, r.kb, r.vt);
     } else if (NB > 2 && younger == 1) {
-      read_slot<LPP, LPP>(ka, va, r.kb, r.v);
+      read_slot<LPP, LPP>(ka, va, r.kb, r.vt);
     } else if (NB > 3 && younger == 2) {
-      read_slot<LPP, 2 * LPP>(ka, va, r.kb, r.v);
+      read_slot<LPP, 2 * LPP>(ka, va, r.kb, r.vt);
     } else {
-      read_slot<LPP, 0>(ka, va, r.kb, r.v);
+      read_slot<LPP, 0>(ka, va, r.kb, r.vt);
     }
     r.ntok = ntok_ring[sl];
     r.lp = lp_ring[sl];
     return r;
   };
 
-  float* sp = s_p[wave];
-
   auto compute_page = [&](Page& r) {
     if (app_owner && r.lp == app_page) {  // the new token's page: its slot from registers
 #pragma unroll
       for (int kk = 0; kk < NKI; ++kk) r.kb[kk] = t16 == app_slot ? k_tok[kk] : r.kb[kk];
 #pragma unroll
-      for (int i = 0; i < NVI; ++i)
-        r.v[i] = i * TPI + vr == app_slot ? v_tok : r.v[i];
+      for (int T = 0; T < NT; ++T)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t& w = r.vt[T][j / 2];
+          const uint32_t keep = (j & 1) ? 0x0000ffffu : 0xffff0000u;
+          const uint32_t put = (j & 1) ? (v_col[T] << 16) : v_col[T];
+          w = 4 * hq + j == app_slot ? ((w & keep) | put) : w;
+        }
     }
+    // S^T = K Q^T: lane l gets head t16 and tokens 4 hq .. +3.
     floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kk = 0; kk < NKI; ++kk) c = mfma_16x16x32<DT>(qa[kk], r.kb[kk], c);
+    for (int kk = 0; kk < NKI; ++kk) c = mfma_16x16x32<DT>(r.kb[kk], qa[kk], c);
     // logits, log2 domain, masked by select (never by multiply: tails may
-    // hold NaN)
-    const bool tok_ok = t16 < r.ntok;
+    // hold NaN); padding heads (t16 >= G) are masked too
+    const bool head_ok = t16 < G;
     float x[4];
     bool need = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = tok_ok && (4 * hq + i < G);
+      const bool ok = head_ok && 4 * hq + i < r.ntok;
       x[i] = ok ? c[i] * a.scale_log2 : -INFINITY;
-      need |= x[i] > mref[i] + kTau;
+      need |= x[i] > mref + kTau;
     }
     if (__any(need)) {
-      float alpha[4];
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = swap32_max(swap16_max(mx));  // over the head's 16 tokens
+      const float mn = fmaxf(mref, mx);
+      const float al = fast_exp2(mref - mn);
+      lsum *= al;
+      mref = mn;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mn = fmaxf(mref[i], row16_max(x[i]));
-        alpha[i] = fast_exp2(mref[i] - mn);
-        lsum[i] *= alpha[i];
-        mref[i] = mn;
-      }
+      for (int T = 0; T < NT; ++T)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float al = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(alpha[h % 4]), 16 * (h / 4)));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-      }
+        for (int i = 0; i < 4; ++i) acc[T][i] *= al;
     }
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(x[i] - mref[i]);
-      lsum[i] += p[i];
+      p[i] = fast_exp2(x[i] - mref);
+      lsum += p[i];
     }
-    if (hq < GR) {
-      if constexpr (G >= 4) {
-        *(float4*)(sp + t16 * G + 4 * hq) = make_float4(p[0], p[1], p[2], p[3]);
-      } else {
+    // P^T in the B-operand layout of the 16x16x32 product, as two 16-bit
+    // parts: k = 8 hq + j holds the rounded weight of token 4 hq + j (j < 4)
+    // or its rounding residual (j >= 4), so the product carries P to ~2^-18.
+    const uint32_t h01 = pack2<DT>(p[0], p[1]), h23 = pack2<DT>(p[2], p[3]);
+    float r0, r1, r2, r3;
+    unpack2<DT>(h01, r0, r1);
+    unpack2<DT>(h23, r2, r3);
+    const u32x4 pt = {h01, h23, pack2<DT>(p[0] - r0, p[1] - r1), pack2<DT>(p[2] - r2, p[3] - r3)};
+    if (r.ntok < P) {  // wave-uniform: only a row's last page is partial
 #pragma unroll
-        for (int i = 0; i < G; ++i) sp[t16 * G + i] = p[i];
-      }
+      for (int T = 0; T < NT; ++T)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t& w = r.vt[T][j / 2];
+          const uint32_t keep = (j & 1) ? 0x0000ffffu : 0xffff0000u;
+          w = 4 * hq + j < r.ntok ? w : (w & keep);
+        }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int i = 0; i < NVI; ++i) {
-      const int t = i * TPI + vr;
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = sp[t * G + h];
-      float vf[8];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) unpack2<DT>(r.v[i][w], vf[2 * w], vf[2 * w + 1]);
-      if (r.ntok < P) {  // wave-uniform: only a row's last page is partial
-        const bool valid = t < r.ntok;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.0f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    for (int T = 0; T < NT; ++T)
+      acc[T] = mfma_16x16x32<DT>(u32x4{r.vt[T][0], r.vt[T][1], r.vt[T][0], r.vt[T][1]}, pt, acc[T]);
   };
 
   // Software pipeline over the LDS ring: the loads of the next NB-1 pages
@@ -920,66 +956,17 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   }
 
   // ---- combine the wave states, then the workgroup's waves ----
-  // l: sum over the 16 tokens of each MFMA row; acc: over the V rows (lane
-  // bits log2(VL) .. 5). The acc sums pair up values so that every exchange
-  // moves two of them: with x and y in the two operands, permlane16_swap
-  // leaves rows (x0, y0, x2, y2) and (x1, y1, x3, y3), whose sum holds x's
-  // and y's row-pair sums; permlane32_swap on two such registers leaves
-  // rows (x0, x1, y0, y1) and (x2, x3, y2, y3), whose sum holds four full
-  // sums, one per 16-lane row. Value v[4j + r] ends in row r of red[j], and
-  // v is the flattened acc[G][8] taken row-major by destination row, so row
-  // r holds 2G consecutive entries of it. Each sum adds (row 0 + row 1) +
-  // (row 2 + row 3), after the bit-3 DPP step when VL = 8.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lsum[i] = row16_sum(lsum[i]);
-  constexpr int NR = 2 * G;  // sums per 16-lane row
-  float red[NR];
-  {
-    float v[4 * NR];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int j = 0; j < NR; ++j) {
-        const int idx = r * NR + j;  // into the flattened acc[G][8]
-        v[4 * j + r] = acc[idx / 8][idx % 8];
-      }
-    if constexpr (VL == 8) {
-#pragma unroll
-      for (int k = 0; k < 4 * NR; ++k) v[k] += dpp_mov<0x128>(v[k]);
-    }
-    float z[2 * NR];
-#pragma unroll
-    for (int i = 0; i < 2 * NR; ++i) {
-      const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * i]),
-                                                      __float_as_uint(v[2 * i + 1]), false, false);
-      z[i] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  // l: sum over the four token rows of head t16; the O^T tiles already hold
+  // full sums over the wave's tokens. Lanes of real heads write their state.
+  lsum = swap32_add(swap16_add(lsum));
+  if (t16 < G) {
+    if (hq == 0) {
+      s_m[wave][t16] = mref;
+      s_l[wave][t16] = lsum;
     }
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[2 * j]),
-                                                      __float_as_uint(z[2 * j + 1]), false, false);
-      red[j] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-    }
-  }
-  // Each row's first lane writes its own heads. (A readlane from another
-  // lane inside a lane-0-only branch is not safe: the compiler may sink the
-  // last step of the row sum into the branch, leaving the other lane's
-  // value unfinished.)
-  if (t16 == 0 && hq < GR) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * hq + i < G) {
-        s_m[wave][4 * hq + i] = mref[i];
-        s_l[wave][4 * hq + i] = lsum[i];
-      }
-  }
-  if (t16 < VL) {  // with VL = 8, lanes 8..15 of a row hold copies
-    const int r = lane >> 4;
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      const int idx = r * NR + j;
-      s_acc[wave * SLOT_WORDS + (idx / 8) * D + t16 * 8 + idx % 8] = red[j];
-    }
+    for (int T = 0; T < NT; ++T)
+      *reinterpret_cast<floatx4*>(s_acc + wave * SLOT_WORDS + t16 * D + 16 * T + 4 * hq) = acc[T];
   }
   }  // non-empty range
   __syncthreads();
