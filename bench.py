@@ -571,9 +571,11 @@ def replicate(dev, name_touched_bytes, replicas=0):
     return n
 
 
-def config_line(P, name, seed, steps, warmup, ramp_ms, ev, modes):
+def config_line(P, name, seed, steps, warmup, ramp_ms, ev, modes, stream=True):
     """Time one workload in each of `modes` (lighter than the headline: no
-    per-step markers); returns a dict per mode with the policy's choice."""
+    per-step markers); returns a dict per mode with the policy's choice and,
+    with `stream`, the plain streaming read of the same K/V bytes timed in
+    the same run (each mode's time over it in `over_stream`)."""
     import torch
     spec, dev, _ = make_inputs(name, seed, "cuda")
     touched = int(np.sum(dev["seq_lens_host"])) * spec.num_kv_heads * spec.head_dim * 4
@@ -599,6 +601,13 @@ def config_line(P, name, seed, steps, warmup, ramp_ms, ev, modes):
             entry["partial_kernel_frac"] = round(part / (r["step_us"] * 1e-6) / 1e9 /
                                                  PEAK_HBM_GBPS, 4)
         out[mode] = entry
+    if stream:
+        kv = int(st["kv_tokens"]) * spec.num_kv_heads * spec.head_dim * 4
+        sc = stream_ceiling(P, dev, kv, steps, ramp_ms, ev)
+        if sc is not None:
+            out["stream_ceiling"] = sc
+            for mode in modes:
+                out[mode]["over_stream"] = round(out[mode]["us_per_step"] / sc["us"], 3)
     del dev
     torch.cuda.empty_cache()
     return out
@@ -853,9 +862,10 @@ def main():
         # batch-4 regime question (unsplit vs split vs work queue, and the
         # policy's pick), measured in the same run.
         cfgs = {"mixed8": config_line(P, "mixed8", seed, a.steps, a.warmup, a.ramp_ms, ev,
-                                      ["auto"]),
+                                      ["auto"], stream=not a.no_stream),
                 "b4": config_line(P, "b4", seed, a.steps, a.warmup, a.ramp_ms, ev,
-                                  ["unsplit", "split", "workqueue", "auto"])}
+                                  ["unsplit", "split", "workqueue", "auto"],
+                                  stream=not a.no_stream)}
         b4 = cfgs["b4"]
         timed = {m: b4[m]["us_per_step"] for m in ("unsplit", "split", "workqueue")}
         b4["auto_pick"] = b4["auto"]["resolved"]
