@@ -563,8 +563,8 @@ __global__ __launch_bounds__(kThreads, 2) void partial_kernel(
   constexpr int NKI = D / 32;     // K: 1 KiB DMA runs per page = MFMA steps
   constexpr int RB = D * 2;       // bytes per token row
   constexpr int NCH = RB / 16;    // 16-byte chunks per token row
-  constexpr int VL = D / 8;       // lanes per token in the V layout
-  constexpr int TPI = 64 / VL;    // tokens per V load instruction
+  constexpr int VL = D / 8;       // 16-byte pieces (lanes) per token row
+  constexpr int TPI = 64 / VL;    // token rows per 1 KiB load instruction
   constexpr int NVI = P / TPI;    // V loads per lane per page
   constexpr int TILE = P * D;     // elements of one (page, KV head) tile
   constexpr int NT = D / 16;      // 16-column tiles of the P.V product
@@ -630,8 +630,13 @@ __global__ __launch_bounds__(kThreads, 2) void partial_kernel(
     pe = 0x7fffffff;
     row = {0, 0};  // unsplit: no merge
   }
-  const int t16 = lane & 15;   // token of this lane in the MFMA result
-  const int hq = lane >> 4;    // head quad of this lane in the MFMA result
+  // Lane roles: in the logits product this lane loads K row (token) t16;
+  // in the S^T and O^T results it holds head t16, and tokens 4 hq .. +3
+  // (S^T) or columns 16 T + 4 hq .. +3 (O^T); in MFMA operands hq picks the
+  // lane's block along k. vr: the token row of the lane's 16-byte piece in
+  // a 1 KiB row-major load (the new token's pool write).
+  const int t16 = lane & 15;
+  const int hq = lane >> 4;
   const int vr = lane / VL;
 
   // Q^T as the MFMA B operand: column t16 = head t16 of the group, k = d in
