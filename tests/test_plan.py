@@ -334,6 +334,25 @@ def test_static_entry_point_refuses_plans_beyond_its_scratch():
     P.pkv_plan_destroy(h)
 
 
+@pytest.mark.parametrize("args", [
+    (None, 16, 16, 2, 4),   # a null buffer
+    (16, 16, 24, 2, 4),     # size not a multiple of 16
+    (16, 16, -16, 2, 4),    # negative size
+    (16, 16, 16, 0, 4),     # no workgroups
+    (8, 16, 16, 2, 4),      # a buffer not 16-byte aligned
+    (16, 16, 16, 2, 2),     # a sink not 4-byte aligned
+])
+def test_stream_read_rejects_bad_arguments_before_any_device_call(args):
+    # Fake, never-dereferenced addresses: the checks come before the launch,
+    # so this runs on the CPU.
+    from paged_kv_gqa_04_amd import _pkv
+    a, b, n, grid, sink = args
+    ptr = lambda x: None if x is None else ctypes.c_void_p(0x10000 + x)
+    st = _pkv.LIB.pkv_stream_read(ptr(a), ptr(b), n, grid, ptr(sink), None)
+    assert st == P.PKV_ERR_INVALID
+    assert "stream read" in _pkv.pkv_last_error()
+
+
 def test_static_scratch_size_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define PKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
