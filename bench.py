@@ -628,6 +628,21 @@ def host_info():
                     break
     except OSError:  # pragma: no cover
         pass
+    import subprocess
+    try:  # lscpu's view of the same CPU: model, family and topology
+        text = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        keys = {"Model name": "model_name", "CPU family": "cpu_family", "Model": "model",
+                "Socket(s)": "sockets", "Core(s) per socket": "cores_per_socket",
+                "Thread(s) per core": "threads_per_core", "CPU(s)": "cpus"}
+        lscpu = {}
+        for line in text.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in keys:
+                lscpu[keys[k.strip()]] = v.strip()
+        if lscpu:
+            info["lscpu"] = lscpu
+    except (OSError, subprocess.SubprocessError):  # pragma: no cover
+        pass
     return info
 
 
