@@ -188,6 +188,43 @@ def test_shapes_and_ragged_tails(dtype, G, Hkv, d, mode):
     assert (got[0] == 0).all()  # empty row -> zeros
 
 
+def _random_cases(n, seed=20260705):
+    """Seeded random small cases across every built shape: batch 1..6,
+    lengths drawn from edge values (0, 1, page boundaries) and uniform
+    ones, G in {1, 2, 4, 8}, d in {64, 128}, both dtypes, every mode and
+    both merge paths, with chunk / split counts that force several ranges
+    per row."""
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129]
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 7))
+        lens = [int(rng.choice(edge)) if rng.random() < 0.5 else int(rng.integers(1, 1500))
+                for _ in range(B)]
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        dtype = W.BF16 if rng.random() < 0.5 else W.F16
+        mode = str(rng.choice(["unsplit", "split", "workqueue", "bucketed", "auto"]))
+        merge = "kernel" if (mode == "bucketed" or rng.random() < 0.3) else "fused"
+        splits = int(rng.integers(1, 9)) if mode == "split" else 0
+        chunk = int(rng.integers(1, 13)) if mode in ("workqueue", "bucketed") else 0
+        out.append(dict(lens=lens, G=G, Hkv=Hkv, d=d, dtype=dtype, mode=mode, merge=merge,
+                        splits=splits, chunk=chunk, seed=int(rng.integers(1, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_random_small_cases(k):
+    c = _random_cases(40)[k]
+    case = _mini(c["lens"], G=c["G"], Hkv=c["Hkv"], d=c["d"], dtype=c["dtype"], seed=c["seed"])
+    got = run_case(case, mode=c["mode"], num_splits=c["splits"], chunk_pages=c["chunk"],
+                   merge=c["merge"])
+    assert_parity(got, O.decode_case(case), str(c))
+    empty = [b for b, n in enumerate(c["lens"]) if n == 0]
+    assert all((got[b] == 0).all() for b in empty)
+
+
 @pytest.mark.parametrize("mode", ["unsplit", "split", "workqueue", "auto"])
 def test_all_rows_empty(mode):
     c = _mini([0, 0, 0])
