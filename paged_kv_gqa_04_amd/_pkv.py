@@ -175,8 +175,22 @@ def make_opts(mode="auto", num_splits=0, chunk_pages=0, num_cus=0,
                     int(queue_seed) & 0xFFFFFFFF, mg)
 
 
+_I32_ARRAY_TYPES: dict = {}
+
+
 def _lens(seq_lens_host):
-    arr = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    """The lengths as a contiguous int32 array and a pointer to it. A
+    writable contiguous int32 ndarray (what a serving loop re-plans with
+    every step) is passed through its buffer without a copy; anything else
+    is converted first."""
+    a = seq_lens_host
+    if type(a) is np.ndarray and a.dtype == np.int32 and a.flags.c_contiguous \
+            and a.flags.writeable and a.size:
+        t = _I32_ARRAY_TYPES.get(a.size)
+        if t is None:
+            t = _I32_ARRAY_TYPES[a.size] = C.c_int32 * a.size
+        return a, t.from_buffer(a)
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
     return arr, arr.ctypes.data_as(C.POINTER(C.c_int32))
 
 

@@ -88,8 +88,8 @@ struct pkv_plan {
   void* pinned = nullptr;  // pinned staging of [items | meta]: the image last copied
   size_t pinned_bytes = 0;
   int64_t copied_bytes = 0;         // length of that image (0: none copied yet)
-  std::vector<char> image_scratch;  // a re-planned image, compared with the copied one
-  std::vector<char> static_image;   // the upload image, for pkv_decode_static (filled by build)
+  std::vector<char> static_image;  // the upload image as last built (pkv_decode_static copies
+                                   // it; a re-plan compares it with the copied one)
   void* upload_event = nullptr;  // hipEvent_t of the last upload copy
   int device = -1;
 };

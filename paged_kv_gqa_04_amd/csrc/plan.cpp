@@ -29,7 +29,6 @@
 #include <functional>
 #include <map>
 #include <new>
-#include <set>
 
 #include "pkv_internal.h"
 
@@ -80,6 +79,34 @@ int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t Hkv, int32_t num_cu
   c = align_up(c, kWavesPerGroup);
   while (c < kMaxChunkPages && items_at(lens, Hkv, c) > target) c += kWavesPerGroup;
   return (int32_t)c;
+}
+
+// Stable order by range length, longest first (items of one length keep
+// their order): a counting placement, since lengths are bounded by the
+// range size; very long ranges fall back to a stable sort.
+void longest_first(std::vector<Item>& items) {
+  constexpr int32_t kCountingMax = 4096;
+  int32_t maxlen = 0;
+  for (const Item& it : items) maxlen = std::max(maxlen, it.page_end - it.page_begin);
+  if (maxlen > kCountingMax) {
+    std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+      return (a.page_end - a.page_begin) > (b.page_end - b.page_begin);
+    });
+    return;
+  }
+  thread_local std::vector<int32_t> start;
+  thread_local std::vector<Item> sorted;
+  start.assign((size_t)maxlen + 1, 0);
+  for (const Item& it : items) ++start[it.page_end - it.page_begin];
+  int32_t off = 0;
+  for (int32_t len = maxlen; len >= 0; --len) {
+    const int32_t c = start[len];
+    start[len] = off;
+    off += c;
+  }
+  sorted.resize(items.size());
+  for (const Item& it : items) sorted[start[it.page_end - it.page_begin]++] = it;
+  items.swap(sorted);
 }
 
 uint64_t splitmix64(uint64_t& s) {
@@ -151,7 +178,10 @@ pkv_status build(pkv_plan& p) {
 
   int64_t total_pages = 0, kv_tokens = 0;
   int32_t max_pages = 0, active = 0;
-  std::set<int32_t> distinct;
+  // Re-planning runs every step: scratch buffers keep their capacity per
+  // thread, so a re-plan allocates nothing once warmed up.
+  thread_local std::vector<int32_t> nonzero;
+  nonzero.clear();
   bool same_len = true;
   for (int32_t b = 0; b < B; ++b) {
     int32_t n = p.seq_lens[b];
@@ -160,10 +190,13 @@ pkv_status build(pkv_plan& p) {
     max_pages = std::max(max_pages, pages_of(n));
     if (n > 0) {
       ++active;
-      distinct.insert(n);
+      nonzero.push_back(n);
     }
     if (pages_of(n) != pages_of(p.seq_lens[0])) same_len = false;
   }
+  std::sort(nonzero.begin(), nonzero.end());
+  const int32_t distinct_lengths =
+      (int32_t)(std::unique(nonzero.begin(), nonzero.end()) - nonzero.begin());
 
   // ---- mode ----
   int32_t mode = p.opts.mode;
@@ -199,7 +232,7 @@ pkv_status build(pkv_plan& p) {
   p.mode = mode;
   p.split_chunk = 0;
   p.kv_tokens = kv_tokens;
-  p.bucket_launches = 2 * (int32_t)distinct.size();
+  p.bucket_launches = 2 * distinct_lengths;
 
   int64_t num_slots = 0;
   if (mode == PKV_MODE_UNSPLIT) {
@@ -310,9 +343,7 @@ pkv_status build(pkv_plan& p) {
     if (p.opts.queue_seed == 0) {
       // Longest ranges first: the hardware hands workgroups out in launch
       // order, so this is greedy longest-processing-time scheduling.
-      std::stable_sort(p.items.begin(), p.items.end(), [](const Item& a, const Item& b) {
-        return (a.page_end - a.page_begin) > (b.page_end - b.page_begin);
-      });
+      longest_first(p.items);
     } else {
       uint64_t st = p.opts.queue_seed;
       for (size_t i = p.items.size(); i > 1; --i)
@@ -477,11 +508,8 @@ pkv_status pkv_plan_update(pkv_plan* p, const int32_t* seq_lens_host) {
   if (need > 0 && (!p->workspace || (uintptr_t)p->workspace % 256 != 0 ||
                    need > (int64_t)p->workspace_bytes))
     return st;
-  if (nb > 0) {
-    p->image_scratch.resize((size_t)nb);
-    pkv::write_upload_image(*p, p->image_scratch.data());
-    if (std::memcmp(p->image_scratch.data(), p->pinned, (size_t)nb) != 0) return st;
-  }
+  // build() has just written the new image (static_image).
+  if (nb > 0 && std::memcmp(p->static_image.data(), p->pinned, (size_t)nb) != 0) return st;
   p->uploaded = true;
   return st;
 }

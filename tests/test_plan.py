@@ -120,6 +120,26 @@ def test_workqueue_partitions_rows_without_empty_items(lens, chunk):
     assert st["num_items"] == sum(Hkv * math.ceil(((int(n) + 15) // 16) / ck) for n in lens)
 
 
+@pytest.mark.parametrize("lens,chunk", [
+    ([256, 1000, 5000, 300, 17, 9000, 0, 4096], 16),  # short ranges: counting placement
+    ([100000, 70000, 0, 90001, 12], 5000),            # ranges past 4096 pages: stable sort
+])
+def test_workqueue_order_is_stable_longest_first(lens, chunk):
+    # Longest range first; ranges of one length keep the order they are
+    # emitted in: by sequence, then KV head, then range (zero-fill items of
+    # empty rows, no pages, last).
+    Hkv = 3
+    h = plan(lens, "workqueue", chunk=chunk, Hq=6, Hkv=Hkv)
+    items = P.pkv_plan_queue_get(h, len(lens), Hkv)[0]
+    lengths = items[:, 2] - items[:, 1]
+    assert (np.diff(lengths) <= 0).all()
+    for n in np.unique(lengths):
+        grp = items[lengths == n]
+        emitted = [(bg, pb) for bg, pb in zip(grp[:, 0], grp[:, 1])]
+        assert emitted == sorted(emitted)
+    P.pkv_plan_destroy(h)
+
+
 def test_workqueue_runs_longest_ranges_first_and_shuffles_on_request():
     lens = [256, 1000, 5000, 300, 17, 9000]
     h = plan(lens, "workqueue", chunk=16)
