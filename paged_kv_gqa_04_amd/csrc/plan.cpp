@@ -434,7 +434,11 @@ void set_error(const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_error = buf;
+  try {
+    g_error = buf;
+  } catch (...) {  // out of host memory: the message is lost, nothing is thrown
+    g_error.clear();
+  }
 }
 
 void clear_error() { g_error.clear(); }
@@ -470,8 +474,13 @@ pkv_status pkv_plan_create(const pkv_shape* shape, const int32_t* seq_lens_host,
       return st;
     }
   }
-  p->seq_lens.assign(seq_lens_host, seq_lens_host + shape->batch);
-  st = pkv::build(*p);
+  try {  // host vectors grow here; no exception crosses the C ABI
+    p->seq_lens.assign(seq_lens_host, seq_lens_host + shape->batch);
+    st = pkv::build(*p);
+  } catch (const std::bad_alloc&) {
+    pkv::set_error("out of host memory");
+    st = PKV_ERR_INVALID;
+  }
   if (st != PKV_OK) {
     delete p;
     return st;
@@ -489,10 +498,15 @@ pkv_status pkv_plan_update(pkv_plan* p, const int32_t* seq_lens_host) {
   pkv_status st = pkv::validate(&p->shape, seq_lens_host);
   if (st != PKV_OK) return st;
   pkv::wait_upload(p);
-  p->seq_lens.assign(seq_lens_host, seq_lens_host + p->shape.batch);
   const bool was_uploaded = p->uploaded;
   p->uploaded = false;  // also after a failed re-plan: decode refuses until a new upload
-  st = pkv::build(*p);
+  try {  // host vectors may grow here; no exception crosses the C ABI
+    p->seq_lens.assign(seq_lens_host, seq_lens_host + p->shape.batch);
+    st = pkv::build(*p);
+  } catch (const std::bad_alloc&) {
+    pkv::set_error("out of host memory");
+    st = PKV_ERR_INVALID;
+  }
   if (st != PKV_OK || !was_uploaded) return st;
   // The workspace still holds the previous image. When the new plan's image
   // is byte for byte the same (the usual case when no row gained or lost a

@@ -66,8 +66,14 @@ pkv_status pkv_pool_create(int32_t num_pages, pkv_pool** out_pool) {
     set_error("out of host memory");
     return PKV_ERR_INVALID;
   }
-  p->taken.assign((size_t)num_pages, 0);
-  p->free_stack.resize((size_t)num_pages);
+  try {  // no exception crosses the C ABI
+    p->taken.assign((size_t)num_pages, 0);
+    p->free_stack.resize((size_t)num_pages);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    set_error("out of host memory");
+    return PKV_ERR_INVALID;
+  }
   for (int32_t i = 0; i < num_pages; ++i) p->free_stack[(size_t)i] = num_pages - 1 - i;
   *out_pool = p;
   return PKV_OK;
