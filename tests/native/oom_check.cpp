@@ -2,7 +2,8 @@
 // status, never as an exception across the C ABI: a global operator new
 // that throws once, after a chosen number of allocations, is armed before
 // each call, and the failure point is walked over every allocation the
-// call makes. Built with plan.cpp and pool.cpp (no HIP kernels) by
+// call makes. It also counts allocations over warmed-up re-plans, which
+// must make none. Built with plan.cpp and pool.cpp (no HIP kernels) by
 // tests/test_host_sanitize.py. Exits non-zero on a failed check; an
 // escaping exception would terminate the program instead.
 #include <cstdio>
@@ -23,6 +24,7 @@ void release_device_resources(pkv_plan*) {}
 
 static long g_left = -1;  // allocations before the one that fails; -1: none fails
 static long g_failed = 0;
+static long g_count = 0;  // allocations made
 
 void* operator new(std::size_t n) {
   if (g_left == 0) {
@@ -31,6 +33,7 @@ void* operator new(std::size_t n) {
     throw std::bad_alloc();
   }
   if (g_left > 0) --g_left;
+  ++g_count;
   void* p = std::malloc(n ? n : 1);
   if (!p) throw std::bad_alloc();
   return p;
@@ -131,6 +134,27 @@ int main() {
       continue;
     }
     CHECK(pool == nullptr);
+  }
+  // Re-planning allocates nothing once warmed up: lengths that move inside
+  // their pages, and rows gaining or losing pages within the sizes already
+  // seen, in every mode.
+  for (int mode : {PKV_MODE_AUTO, PKV_MODE_SPLIT, PKV_MODE_WORKQUEUE, PKV_MODE_BUCKETED}) {
+    pkv_opts o{};
+    o.mode = mode;
+    o.chunk_pages = 8;
+    o.num_cus = 256;
+    pkv_plan* p = nullptr;
+    CHECK(pkv_plan_create(&s, lens.data(), &o, &p) == PKV_OK);
+    std::vector<int32_t> step(lens);
+    for (int warm = 0; warm < 2; ++warm)
+      for (int i = 0; i < 64; ++i) {
+        for (size_t b = 0; b < step.size(); ++b) step[b] = lens[b] + (int32_t)((i * 7 + b) % 40);
+        if (i == 0 && warm == 1) g_count = 0;  // second pass: count
+        CHECK(pkv_plan_update(p, step.data()) == PKV_OK);
+      }
+    if (mode != PKV_MODE_BUCKETED)  // the comparator's buckets are rebuilt from maps
+      CHECK(g_count == 0);
+    pkv_plan_destroy(p);
   }
   CHECK(handled > 20);
   std::printf("allocation failures handled: %ld\n", handled);
