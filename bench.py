@@ -527,7 +527,7 @@ def serve_loop(P, name, seed, mode, steps, warmup):
             "steps_with_queue_copy": int(copies), "steps_with_table_copy": int(table_updates)}
 
 
-def stream_ceiling(P, dev, kv_bytes, steps, ramp_ms, ev, grids=(512, 1024, 2048)):
+def stream_ceiling(P, dev, kv_bytes, steps, ramp_ms, ev, grids=(256, 512, 768, 1024, 2048)):
     """The same number of K/V bytes as one step, read once by a plain
     streaming kernel (half from each pool, rotating over the same pool
     copies as the decode): the HBM ceiling a one-pass read of these bytes
