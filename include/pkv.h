@@ -78,7 +78,7 @@ typedef enum pkv_dtype { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
 /* Dispatch modes (PersistentKV explainer, Methodology 2: the policy routes a
  * step to one of several execution paths by batch size and length).
  *   UNSPLIT    one workgroup per (sequence, KV head); writes out; 1 launch.
- *   SPLIT      rectangular grid B x Hkv x S; row b uses
+ *   SPLIT      rectangular grid S x Hkv x B (x, y, z); row b uses
  *              chunk_b = ceil(pages_b / S) pages per range; cells past the
  *              row's last range write a neutral state; partial + merge.
  *   WORKQUEUE  1-D grid over the non-empty (sequence, KV head, range) items
@@ -184,7 +184,7 @@ typedef struct pkv_plan_stats {
 
 typedef struct pkv_workspace_layout {
   int64_t items_offset;  /* int32x8 {b*Hkv+g, page_begin, page_end, slot,
-                            row_base, row_count, 0, 0}: row_base / row_count
+                            row_base, row_count, b, g}: row_base / row_count
                             are the first slot and the range count of
                             (b, g); a zero-fill item has slot -1 */
   int64_t meta_offset;   /* int32x2 per sequence (WORKQUEUE, BUCKETED);
@@ -213,8 +213,10 @@ typedef struct pkv_plan pkv_plan; /* opaque; host-owned */
  *   out_plan       receives the new plan; *out_plan is NULL on failure.
  * Errors: PKV_ERR_INVALID for null pointers, negative sizes, Hq % Hkv != 0,
  * N_b < 0 or N_b > block_table_stride * page_size; PKV_ERR_UNSUPPORTED for a
- * page size, head_dim, G or dtype this build has no kernel for; PKV_ERR_HIP
- * if num_cus is 0 and the device cannot be queried. Host-only: calls no HIP
+ * page size, head_dim, G or dtype this build has no kernel for, and for
+ * PKV_MODE_SPLIT with batch or num_kv_heads above 65535 (grid dimensions;
+ * AUTO then picks the work queue); PKV_ERR_HIP if num_cus is 0 and the
+ * device cannot be queried. Host-only: calls no HIP
  * function unless num_cus is 0. */
 pkv_status pkv_plan_create(const pkv_shape* shape, const int32_t* seq_lens_host,
                            const pkv_opts* opts, pkv_plan** out_plan);

@@ -597,20 +597,22 @@ __global__ __launch_bounds__(kThreads, 2) void partial_kernel(
   SeqMeta row;         // (first slot, range count) of (b, g), for the merge
   if (a.mode == PKV_MODE_WORKQUEUE) {
     const Item it = a.items[blockIdx.x];
-    b = it.bg / Hkv;
-    g = it.bg - b * Hkv;
+    b = it.b;
+    g = it.g;
     pb = it.page_begin;
     pe = it.page_end;
     slot = it.slot;
     row = {it.row_base, it.row_count};
     early = true;
   } else if (a.mode == PKV_MODE_SPLIT) {
+    // Grid S x Hkv x B, so (range, KV head, sequence) come without a
+    // division; the linear workgroup order is still range-fastest.
     const int S = a.num_splits;
-    const int cell = blockIdx.x;
-    const int s = cell % S;
-    const int bg = cell / S;
-    b = bg / Hkv;
-    g = bg - b * Hkv;
+    const int s = blockIdx.x;
+    g = blockIdx.y;
+    b = blockIdx.z;
+    const int bg = b * Hkv + g;
+    const int cell = bg * S + s;
     if (a.split_chunk > 0) {  // every row has this range size
       pb = s * a.split_chunk;
       pe = pb + a.split_chunk;
@@ -1233,7 +1235,10 @@ pkv_status decode_impl(const pkv_plan* p, const void* q, const void* k_pool, con
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);
   } else {
     if (p->grid > 0) {
-      lp(dim3(p->grid), stream, pp);
+      const dim3 grid = p->mode == PKV_MODE_SPLIT
+                            ? dim3(p->num_splits, s.num_kv_heads, s.batch)  // = p->grid workgroups
+                            : dim3(p->grid);
+      lp(grid, stream, pp);
       if ((e = hipGetLastError()) != hipSuccess) return hip_fail("partial kernel launch", e);
     }
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail("hipEventRecord", e);

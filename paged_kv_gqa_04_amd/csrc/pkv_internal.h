@@ -33,7 +33,7 @@ struct Item {
   int32_t slot;        // partial-state slot this range writes (-1: zero-fill item)
   int32_t row_base;    // first slot of (b, g)
   int32_t row_count;   // ranges of (b, g)
-  int32_t pad0, pad1;
+  int32_t b, g;        // bg split, so the kernel needs no division for it
 };
 static_assert(sizeof(Item) == 32, "item layout");
 

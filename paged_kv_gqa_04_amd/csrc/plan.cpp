@@ -56,6 +56,9 @@ constexpr int kTargetItemsPerCU = 1;
 constexpr int kMaxChunkPages = 512;
 // Smallest range worth a workgroup (pages): two pages per wave.
 constexpr int kMinChunkPages = 2 * kWavesPerGroup;
+// The split grid's y and z dimensions (KV heads, sequences) stay within the
+// smallest grid-dimension limit HIP devices report.
+constexpr int32_t kMaxGridYZ = 65535;
 
 int32_t pages_of(int32_t n) { return (int32_t)ceil_div(n, kPageTokens); }
 
@@ -218,11 +221,17 @@ pkv_status build(pkv_plan& p) {
   if (mode == PKV_MODE_AUTO) {
     if (active == 0 || max_pages <= chunk) {
       mode = PKV_MODE_UNSPLIT;  // every row fits in one item: nothing to merge
-    } else if (same_len) {
+    } else if (same_len && B <= kMaxGridYZ && Hkv <= kMaxGridYZ) {
       mode = PKV_MODE_SPLIT;  // equal rows: the rectangular grid wastes nothing
     } else {
       mode = PKV_MODE_WORKQUEUE;  // ragged rows: only non-empty ranges
     }
+  }
+
+  if (mode == PKV_MODE_SPLIT && (B > kMaxGridYZ || Hkv > kMaxGridYZ)) {
+    set_error("split grid: batch and KV heads must be at most %d each (the work queue has no "
+              "such limit)", kMaxGridYZ);
+    return PKV_ERR_UNSUPPORTED;
   }
 
   p.items.clear();
@@ -292,7 +301,7 @@ pkv_status build(pkv_plan& p) {
             for (int32_t si = 0; si < Sb; ++si)
               p.items.push_back({b * Hkv + g, si * c, std::min(pg, (si + 1) * c),
                                  (int32_t)(num_slots + (int64_t)g * Sb + si),
-                                 (int32_t)(num_slots + (int64_t)g * Sb), Sb, 0, 0});
+                                 (int32_t)(num_slots + (int64_t)g * Sb), Sb, b, g});
           num_slots += (int64_t)Hkv * Sb;
           if (num_slots > INT32_MAX / 2) {
             set_error("bucket plan too large");
@@ -303,7 +312,7 @@ pkv_status build(pkv_plan& p) {
         cmax = std::max(cmax, c);
       } else if (p.fused) {
         for (int32_t b : rows)
-          for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1, 0, 0, 0, 0});
+          for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1, 0, 0, b, g});
         fills += (int32_t)rows.size() * Hkv;
       }
       for (int32_t b : rows) p.rows.push_back(b);
@@ -327,12 +336,12 @@ pkv_status build(pkv_plan& p) {
         for (int32_t si = 0; si < Sb; ++si)
           p.items.push_back({b * Hkv + g, si * chunk, std::min(pg, (si + 1) * chunk),
                              (int32_t)(num_slots + (int64_t)g * Sb + si),
-                             (int32_t)(num_slots + (int64_t)g * Sb), Sb, 0, 0});
+                             (int32_t)(num_slots + (int64_t)g * Sb), Sb, b, g});
       // An empty row has no range; with the merge fused into the partial
       // kernel nothing else would write its (zero) output, so it gets one
       // zero-fill item per KV head (slot -1, no pages).
       if (Sb == 0 && p.fused)
-        for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1, 0, 0, 0, 0});
+        for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1, 0, 0, b, g});
       num_slots += (int64_t)Hkv * Sb;
       smax = std::max(smax, Sb);
       if (num_slots > INT32_MAX / 2) {

@@ -179,6 +179,24 @@ def test_split_grid_counts(lens, S):
     assert P.pkv_plan_stats_get(hk)["launches"] == 2
 
 
+def test_split_grid_dimension_limit():
+    """The split grid is launched S x Hkv x B: past 65535 sequences an
+    explicit split plan is refused, and AUTO plans equal rows as a work
+    queue instead."""
+    B = 65536
+    lens = np.full(B, 16 * 16, np.int32)  # 16 pages per row
+    with pytest.raises(P.PkvError) as e:
+        plan(lens, "split", S=2, Hq=1, Hkv=1, chunk=8)
+    assert e.value.status == P.PKV_ERR_UNSUPPORTED
+    h = plan(lens, "auto", Hq=1, Hkv=1, chunk=8)
+    st = P.pkv_plan_stats_get(h)
+    assert st["mode"] == P.MODES["workqueue"] and st["grid"] == 2 * B
+    P.pkv_plan_destroy(h)
+    h = plan(lens[:65535], "auto", Hq=1, Hkv=1, chunk=8)
+    assert P.pkv_plan_stats_get(h)["mode"] == P.MODES["split"]
+    P.pkv_plan_destroy(h)
+
+
 def test_workqueue_separate_merge_has_no_fill_items():
     lens = [0, 100, 0, 5]
     h = plan(lens, "workqueue", chunk=2, merge="kernel")
@@ -436,13 +454,14 @@ def test_zero_batch_plan():
 @pytest.mark.parametrize("lens", RAGGED)
 def test_items_name_their_row_slots(mode, lens):
     """Each item carries (first slot, range count) of its (b, g) row, equal
-    to what the per-row table says; zero-fill items carry (0, 0)."""
+    to what the per-row table says, and b and g themselves; zero-fill items
+    carry (0, 0) as slot base and count."""
     Hkv = 8
     h = plan(lens, mode)
     items, meta, _ = P.pkv_plan_queue_get(h, len(lens), Hkv, full=True)
-    for bg, p0, p1, slot, base, count, z0, z1 in items:
+    for bg, p0, p1, slot, base, count, ib, ig in items:
         b, g = bg // Hkv, bg % Hkv
-        assert z0 == z1 == 0
+        assert (ib, ig) == (b, g)
         if slot < 0:
             assert (p0, p1, base, count) == (0, 0, 0, 0)
             continue
