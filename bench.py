@@ -15,6 +15,9 @@ is at its steady clocks whatever --warmup is.
 
 The default line also carries: the same K/V bytes read by a plain streaming
 kernel (``stream_ceiling``: the one-pass read ceiling in this run), the
+same tiles read through the block table with the decode's own work split
+and load path but no arithmetic, state or merge (``paged_read``: what the
+paged gather alone costs in this run; per config ``paged_read_us``), the
 mixed batch of 8 and the batch-4 regime (``configs``: mixed8 in the policy's
 mode; b4 unsplit, split, work queue and the policy's pick), and the CPU
 oracle on the host (``cpu_baseline``, with the 64-sequence step
@@ -193,12 +196,14 @@ def ramp(launch, min_ms):
 
 
 def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, merge="fused",
-              ramp_ms=0.0, light=False):
+              ramp_ms=0.0, light=False, paged_read=False):
     """Time `steps` back-to-back decode steps (one event pair around all of
     them: per-step markers would add their own overhead) after a clock ramp
-    of `ramp_ms` and `warmup` more steps; unless `light`, then the same
-    number of steps with markers around the partial kernel alone, and the
-    synchronized wall time with host planning."""
+    of `ramp_ms` and `warmup` more steps; with `paged_read`, then as many
+    back-to-back paged reads with the same plan and pool copies (the gather
+    alone: `paged_read_us`); unless `light`, then the same number of steps
+    with markers around the partial kernel alone, and the synchronized wall
+    time with host planning."""
     import torch
     B = len(dev["seq_lens_host"])
     shape = P.make_shape(B, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
@@ -227,10 +232,13 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
     wall = time.perf_counter() - t0
     step_ms = ev.ms(e_all[0], e_all[1]) / steps
     ev.destroy(e_all)
+    extra = {}
+    if paged_read and stats["mode_name"] != "bucketed":
+        extra["paged_read_us"] = time_paged_read(P, plan, dev, pools, steps, ev)
     if light:
         plan.close()
         return {"stats": stats, "step_us": step_ms * 1e3, "wall_us_per_step": wall / steps * 1e6,
-                "ramp_steps": ramp_steps, "ramp_ms": ramp_done}
+                "ramp_steps": ramp_steps, "ramp_ms": ramp_done, **extra}
     # 2) per-step markers around the partial kernel (includes marker cost)
     evs = ev.create(2 * steps)
     for i in range(steps):
@@ -267,7 +275,31 @@ def time_mode(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, me
         "sync_wall_us_with_plan_copy": float(np.median(sync_copy)) * 1e6,
         "ramp_steps": ramp_steps,
         "ramp_ms": ramp_done,
+        **extra,
     }
+
+
+def time_paged_read(P, plan, dev, pools, steps, ev):
+    """µs per paged read (pkv_paged_read: every K/V tile the decode with
+    `plan` reads, with its work split and load path, nothing else), timed
+    back to back over the same pool copies right after the decode's steps."""
+    import torch
+    sink = torch.zeros(1, dtype=torch.int32, device=dev["q"].device)
+    stream = torch.cuda.current_stream().cuda_stream
+    read = lambda i: P.pkv_paged_read(plan.handle, pools[i % len(pools)][0],
+                                      pools[i % len(pools)][1], dev["block_table"],
+                                      dev["seq_lens"], sink, stream)
+    for i in range(min(steps, 50)):
+        read(i)
+    e = ev.create(2)
+    ev.record(e[0], stream)
+    for i in range(steps):
+        read(i)
+    ev.record(e[1], stream)
+    torch.cuda.synchronize()
+    us = ev.ms(e[0], e[1]) / steps * 1e3
+    ev.destroy(e)
+    return us
 
 
 def time_graph(P, dev, spec, mode, splits, chunk, steps, warmup, replicas, ev, merge="fused"):
@@ -584,7 +616,7 @@ def config_line(P, name, seed, steps, warmup, ramp_ms, ev, modes, stream=True):
     out = {"description": spec.description, "pool_replicas": nrep}
     for mode in modes:
         r = time_mode(P, dev, spec, mode, 0, 0, steps, warmup, nrep, ev, ramp_ms=ramp_ms,
-                      light=True)
+                      light=True, paged_read=True)
         st = r["stats"]
         alg = st["algorithmic_bytes"]
         gbps = alg / (r["step_us"] * 1e-6) / 1e9
@@ -600,6 +632,9 @@ def config_line(P, name, seed, steps, warmup, ramp_ms, ev, modes, stream=True):
         if st["launches"] == 1:  # the launch is the whole step
             entry["partial_kernel_frac"] = round(part / (r["step_us"] * 1e-6) / 1e9 /
                                                  PEAK_HBM_GBPS, 4)
+        if "paged_read_us" in r:
+            entry["paged_read_us"] = round(r["paged_read_us"], 2)
+            entry["over_paged_read"] = round(r["step_us"] / r["paged_read_us"], 3)
         out[mode] = entry
     if stream:
         kv = int(st["kv_tokens"]) * spec.num_kv_heads * spec.head_dim * 4
@@ -786,7 +821,7 @@ def main():
         ablation(P, dev, spec, replicas, ev, a, seed)
         return
     r = time_mode(P, dev, spec, mode, splits, a.chunk, a.steps, a.warmup, replicas, ev, a.merge,
-                  ramp_ms=a.ramp_ms)
+                  ramp_ms=a.ramp_ms, paged_read=not a.no_stream)
     st = r["stats"]
     B = len(dev["seq_lens_host"])
     alg = st["algorithmic_bytes"]
@@ -853,6 +888,10 @@ def main():
         if sc is not None:
             sc["decode_over_stream"] = round(r["step_us"] / sc["us"], 3)
             line["stream_ceiling"] = sc
+    if "paged_read_us" in r:
+        line["paged_read"] = {"us": round(r["paged_read_us"], 2),
+                              "gbps": round(alg / (r["paged_read_us"] * 1e-6) / 1e9, 1),
+                              "decode_over_paged_read": round(r["step_us"] / r["paged_read_us"], 3)}
     if not a.no_auto and mode != "auto":
         ra = time_mode(P, dev, spec, "auto", 0, 0, a.steps, a.warmup, replicas, ev,
                        ramp_ms=a.ramp_ms, light=True)

@@ -412,6 +412,23 @@ pkv_status pkv_decode_static(const pkv_plan* plan, const void* q, const void* k_
 pkv_status pkv_stream_read(const void* a, const void* b, int64_t bytes_each, int32_t grid,
                            void* sink, hipStream_t stream);
 
+/* Measurement aid: read every K and V tile that pkv_decode with this plan
+ * reads (each item's pages of its (sequence, KV head) row through the block
+ * table: PersistentKV explainer, Methodology 1), with the partial kernel's
+ * grid and work split and the same kind of load path (nontemporal 16-byte
+ * direct-to-LDS loads, a two-slot ring per wave), asynchronous on `stream`,
+ * and fold the data into a check word: no q, softmax, state or merge. Timed
+ * beside pkv_decode it gives the cost of the paged gather alone. Arguments
+ * as pkv_decode (k_pool/v_pool 16-byte, block_table/seq_lens 4-byte aligned
+ * device pointers); `sink` is a device word (4-byte aligned) the kernel may
+ * write. A work-queue plan must be uploaded. Errors: PKV_ERR_INVALID (null
+ * or misaligned pointer), PKV_ERR_STATE (work queue not uploaded),
+ * PKV_ERR_UNSUPPORTED (PKV_MODE_BUCKETED, head_dim other than 64 or 128),
+ * PKV_ERR_HIP. */
+pkv_status pkv_paged_read(const pkv_plan* plan, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const int32_t* seq_lens, void* sink,
+                          hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* pkv_status_string(int32_t status);
 

@@ -42,6 +42,7 @@ from ._pkv import (  # noqa: F401
     pkv_decode_marked,
     pkv_decode_static,
     pkv_last_error,
+    pkv_paged_read,
     pkv_plan_create,
     pkv_plan_destroy,
     pkv_plan_layout_get,

@@ -114,6 +114,7 @@ SIGNATURES = {
     "pkv_append": (C.c_int32, [C.POINTER(pkv_shape), _P, _P, _P, _P, _P, _P, _P, _P]),
     "pkv_decode_append": (C.c_int32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "pkv_stream_read": (C.c_int32, [_P, _P, C.c_int64, C.c_int32, _P, _P]),
+    "pkv_paged_read": (C.c_int32, [_P, _P, _P, _P, _P, _P, _P]),
     "pkv_decode_static": (C.c_int32, [_P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -376,6 +377,14 @@ def pkv_append(shape: pkv_shape, k_new, v_new, k_pool, v_pool, block_table, seq_
     _check(LIB.pkv_append(C.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                           _ptr(block_table), _ptr(seq_lens), _ptr(new_seq_lens),
                           _ptr(stream) or None), "pkv_append")
+
+
+def pkv_paged_read(plan: int, k_pool, v_pool, block_table, seq_lens, sink, stream=0) -> None:
+    """Read the K/V tiles ``pkv_decode`` with this plan reads, with its work
+    split and load path and nothing else (measurement aid: the cost of the
+    paged gather alone)."""
+    _check(LIB.pkv_paged_read(plan, _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                              _ptr(seq_lens), _ptr(sink), _ptr(stream) or None), "pkv_paged_read")
 
 
 def pkv_stream_read(a, b, bytes_each: int, grid: int, sink, stream=0) -> None:

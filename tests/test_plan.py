@@ -391,6 +391,33 @@ def test_stream_read_rejects_bad_arguments_before_any_device_call(args):
     assert "stream read" in _pkv.pkv_last_error()
 
 
+def test_paged_read_checks_come_before_any_device_call():
+    """pkv_paged_read refuses bad pointers, the bucketed comparator and a
+    work queue that was never uploaded, and returns at once for an empty
+    grid, all before touching a device (fake, never-dereferenced addresses)."""
+    from paged_kv_gqa_04_amd import _pkv
+    ptr = lambda x: None if x is None else ctypes.c_void_p(0x10000 + x)
+    good = (ptr(0), ptr(16), ptr(32), ptr(48), ptr(64))
+    lens = [300, 1000, 17, 4000]
+    h = plan(lens, "split", S=4)
+    for i, bad in [(0, None), (1, ptr(24)), (2, ptr(34)), (3, None), (4, ptr(66))]:
+        args = list(good)
+        args[i] = bad
+        assert _pkv.LIB.pkv_paged_read(h, *args, None) == P.PKV_ERR_INVALID
+        assert "paged read" in _pkv.pkv_last_error()
+    assert _pkv.LIB.pkv_paged_read(None, *good, None) == P.PKV_ERR_INVALID
+    P.pkv_plan_destroy(h)
+    hb = plan(lens, "bucketed")
+    assert _pkv.LIB.pkv_paged_read(hb, *good, None) == P.PKV_ERR_UNSUPPORTED
+    P.pkv_plan_destroy(hb)
+    hq = plan(lens, "workqueue")
+    assert _pkv.LIB.pkv_paged_read(hq, *good, None) == P.PKV_ERR_STATE
+    P.pkv_plan_destroy(hq)
+    h0 = plan([], "split", S=4)
+    assert _pkv.LIB.pkv_paged_read(h0, *good, None) == P.PKV_OK
+    P.pkv_plan_destroy(h0)
+
+
 def test_static_scratch_size_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define PKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
