@@ -327,21 +327,16 @@ pkv_status build(pkv_plan& p) {
   } else {  // WORKQUEUE
     if (chunk <= 0) chunk = kMinChunkPages;
     int32_t smax = 0;
+    int64_t n_full = 0, n_short = 0, n_fill = 0;
     p.meta.resize(B);
     for (int32_t b = 0; b < B; ++b) {
-      int32_t pg = pages_of(p.seq_lens[b]);
-      int32_t Sb = (int32_t)ceil_div(pg, chunk);
+      const int32_t pg = pages_of(p.seq_lens[b]);
+      const int32_t Sb = (int32_t)ceil_div(pg, chunk);
       p.meta[b] = {(int32_t)num_slots, Sb};
-      for (int32_t g = 0; g < Hkv; ++g)
-        for (int32_t si = 0; si < Sb; ++si)
-          p.items.push_back({b * Hkv + g, si * chunk, std::min(pg, (si + 1) * chunk),
-                             (int32_t)(num_slots + (int64_t)g * Sb + si),
-                             (int32_t)(num_slots + (int64_t)g * Sb), Sb, b, g});
-      // An empty row has no range; with the merge fused into the partial
-      // kernel nothing else would write its (zero) output, so it gets one
-      // zero-fill item per KV head (slot -1, no pages).
-      if (Sb == 0 && p.fused)
-        for (int32_t g = 0; g < Hkv; ++g) p.items.push_back({b * Hkv + g, 0, 0, -1, 0, 0, b, g});
+      const bool short_last = pg % chunk != 0;  // Sb > 0 then
+      n_full += (int64_t)Hkv * (Sb - (short_last ? 1 : 0));
+      n_short += short_last ? Hkv : 0;
+      n_fill += (Sb == 0 && p.fused) ? Hkv : 0;
       num_slots += (int64_t)Hkv * Sb;
       smax = std::max(smax, Sb);
       if (num_slots > INT32_MAX / 2) {
@@ -349,11 +344,39 @@ pkv_status build(pkv_plan& p) {
         return PKV_ERR_INVALID;
       }
     }
-    if (p.opts.queue_seed == 0) {
-      // Longest ranges first: the hardware hands workgroups out in launch
-      // order, so this is greedy longest-processing-time scheduling.
-      longest_first(p.items);
-    } else {
+    // The queue is written in place, longest range first with ranges of one
+    // length in (b, g, range) order: the hardware hands workgroups out in
+    // launch order, so this is greedy longest-processing-time scheduling.
+    // Every range but a row's last is `chunk` pages long, so the order is the
+    // full ranges as generated, then the short last ranges by length, then
+    // the zero-fill items. (An empty row has no range; with the merge fused
+    // into the partial kernel nothing else would write its zero output, so it
+    // gets one zero-fill item per KV head: slot -1, no pages.) Only the short
+    // ranges, at most one per (b, g), are sorted.
+    p.items.resize((size_t)(n_full + n_short + n_fill));
+    thread_local std::vector<Item> tails;
+    tails.clear();
+    Item* full = p.items.data();
+    Item* fill = full + n_full + n_short;
+    for (int32_t b = 0; b < B; ++b) {
+      const int32_t pg = pages_of(p.seq_lens[b]);
+      const int32_t Sb = p.meta[b].splits;
+      for (int32_t g = 0; g < Hkv; ++g) {
+        const int32_t base = p.meta[b].slot_base + g * Sb;
+        for (int32_t si = 0; si < Sb; ++si) {
+          const Item it{b * Hkv + g, si * chunk, std::min(pg, (si + 1) * chunk), base + si, base,
+                        Sb, b, g};
+          if (it.page_end - it.page_begin == chunk)
+            *full++ = it;
+          else
+            tails.push_back(it);
+        }
+        if (Sb == 0 && p.fused) *fill++ = {b * Hkv + g, 0, 0, -1, 0, 0, b, g};
+      }
+    }
+    longest_first(tails);
+    std::copy(tails.begin(), tails.end(), full);
+    if (p.opts.queue_seed != 0) {  // a seeded shuffle of the queue (tests: order independence)
       uint64_t st = p.opts.queue_seed;
       for (size_t i = p.items.size(); i > 1; --i)
         std::swap(p.items[i - 1], p.items[splitmix64(st) % i]);

@@ -140,6 +140,36 @@ def test_workqueue_order_is_stable_longest_first(lens, chunk):
     P.pkv_plan_destroy(h)
 
 
+def test_workqueue_queue_matches_a_stable_sort_of_the_generated_ranges():
+    """The queue equals the (b, g, range)-ordered list of ranges, zero-fill
+    items included, stably sorted by length, longest first (random batches,
+    range sizes and KV-head counts)."""
+    rng = np.random.default_rng(2024)
+    for trial in range(60):
+        B = int(rng.integers(1, 12))
+        Hkv = int(rng.choice([1, 2, 3, 8]))
+        lens = rng.integers(0, 3000, B).astype(np.int32)
+        lens[rng.random(B) < 0.2] = 0
+        chunk = int(rng.choice([8, 12, 16, 40, 64]))
+        h = plan(lens, "workqueue", chunk=chunk, Hq=2 * Hkv, Hkv=Hkv)
+        got = P.pkv_plan_queue_get(h, B, Hkv, full=True)[0].tolist()
+        want, slot = [], 0
+        for b, n in enumerate(lens):
+            pg = (int(n) + 15) // 16
+            S = -(-pg // chunk)
+            for g in range(Hkv):
+                base = slot + g * S
+                for si in range(S):
+                    want.append([b * Hkv + g, si * chunk, min(pg, (si + 1) * chunk), base + si, base,
+                                 S, b, g])
+                if S == 0:
+                    want.append([b * Hkv + g, 0, 0, -1, 0, 0, b, g])
+            slot += Hkv * S
+        want.sort(key=lambda it: -(it[2] - it[1]))  # stable
+        assert got == want, (trial, lens.tolist(), chunk, Hkv)
+        P.pkv_plan_destroy(h)
+
+
 def test_workqueue_runs_longest_ranges_first_and_shuffles_on_request():
     lens = [256, 1000, 5000, 300, 17, 9000]
     h = plan(lens, "workqueue", chunk=16)
