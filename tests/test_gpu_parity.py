@@ -157,6 +157,24 @@ def test_b64_full_size():
 # ----------------------------------------------------------- split counts
 
 
+@pytest.fixture(scope="module")
+def longest_row_case():
+    c = W.make_case_from_lengths("longest_row", [262144, 100], num_q_heads=32, num_kv_heads=8,
+                                 head_dim=128, dtype=W.BF16, seed=3, poison=False)
+    return c, W.case_to_device(c), O.decode_case(c)
+
+
+@pytest.mark.parametrize("mode,S", [("auto", 0), ("unsplit", 0), ("split", 32)])
+def test_longest_row(longest_row_case, mode, S):
+    """A row of 262,144 tokens (16,384 pages: twice the longest row of the
+    batch-of-64 workload) beside a short one: unsplit, each of its
+    workgroups walks 32 staged block-table chunks; in the work queue and
+    the split grid, 32 ranges per (row, KV head) are merged."""
+    c, dev, want = longest_row_case
+    got = run_case(c, dev, mode=mode, num_splits=S)
+    assert_parity(got, want, f"longest row/{mode}/S={S}")
+
+
 @pytest.mark.parametrize("S", [1, 2, 4, 7, 32, 200])
 def test_split_counts(S):
     c = _mini([2000, 300, 16, 1, 4097], seed=S)
