@@ -152,6 +152,8 @@ def kernel_sources() -> bytes:
 TRAFFIC_PROFILES = {
     ("long", "split", 32, "fused"): "partial_kernel_long_split32_traffic.md",
     ("mixed8", "workqueue", 14, "fused"): "partial_kernel_mixed8_workqueue_traffic.md",
+    ("b4", "workqueue", 13, "fused"): "partial_kernel_b4_workqueue_traffic.md",
+    ("b64", "workqueue", 16, "fused"): "partial_kernel_b64_workqueue_traffic.md",
 }
 
 
