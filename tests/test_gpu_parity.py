@@ -157,6 +157,18 @@ def test_b64_full_size():
 # ----------------------------------------------------------- split counts
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.F16])
+@pytest.mark.parametrize("mode,S,chunk", [("auto", 0, 0), ("split", 16, 0), ("workqueue", 0, 32),
+                                          ("unsplit", 0, 0)])
+def test_g8_d64_mid_size(dtype, mode, S, chunk):
+    """The G=8, d=64 kernel on rows of thousands of tokens (many pages per
+    wave, several table chunks per unsplit row, tens of ranges per row to
+    merge), with NaN-poisoned unused pool pages and row tails."""
+    c = _mini([12000, 8000, 3000, 517, 1], G=8, Hkv=4, d=64, dtype=dtype, seed=88)
+    got = run_case(c, mode=mode, num_splits=S, chunk_pages=chunk)
+    assert_parity(got, O.decode_case(c), f"G8/d64/{dtype}/{mode}")
+
+
 @pytest.fixture(scope="module")
 def longest_row_case():
     c = W.make_case_from_lengths("longest_row", [262144, 100], num_q_heads=32, num_kv_heads=8,
