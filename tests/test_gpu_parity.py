@@ -169,6 +169,17 @@ def test_g8_d64_mid_size(dtype, mode, S, chunk):
     assert_parity(got, O.decode_case(c), f"G8/d64/{dtype}/{mode}")
 
 
+@pytest.mark.parametrize("G,Hkv,d,dtype", [(1, 8, 128, W.F16), (2, 4, 64, W.BF16),
+                                           (4, 8, 128, W.F16), (8, 8, 128, W.F16)])
+@pytest.mark.parametrize("mode", ["auto", "split"])
+def test_other_shapes_mid_size(G, Hkv, d, dtype, mode):
+    """Every other built (G, d) and the fp16 caches on rows of thousands of
+    tokens, in the policy's mode and on the split grid."""
+    c = _mini([16384, 5000, 777, 33], G=G, Hkv=Hkv, d=d, dtype=dtype, seed=G * 10 + d)
+    got = run_case(c, mode=mode, num_splits=8 if mode == "split" else 0)
+    assert_parity(got, O.decode_case(c), f"G{G}/Hkv{Hkv}/d{d}/{dtype}/{mode}")
+
+
 @pytest.fixture(scope="module")
 def longest_row_case():
     c = W.make_case_from_lengths("longest_row", [262144, 100], num_q_heads=32, num_kv_heads=8,
